@@ -1,0 +1,182 @@
+/*
+ * libdcptopk — stable global top-K selection for the decode-context-parallel
+ * (DCP) sparse-indexer merge, for AMD Instinct MI355X (gfx950).
+ *
+ * What is computed (vLLM PR #47348, "[Kernel] Optimize CuTeDSL DCP top-k
+ * merge", Summary): every DCP rank holds the local top-K of its 1/DCP shard of
+ * the KV cache; the merge picks, for every query row, the global top-K of the
+ * gathered candidates, ordered by score descending and, among equal scores, by
+ * the lowest global token id, deterministically.  The pack step and the row
+ * chunking follow vLLM PR #59367 ("[Bugfix][Attention] Reserve the sparse
+ * indexer's DCP top-k merge scratch through the workspace manager", Purpose).
+ *
+ * Conventions shared by every entry point:
+ *
+ *  - A candidate is 8 bytes: an fp32 score then an int32 global token id
+ *    (dcp_topk_cand).  Scores are never converted or rounded: every result
+ *    copies the score's bits.
+ *  - Order: scores compare through the order-preserving 32-bit key of their
+ *    bits (IEEE 754 totalOrder: -NaN < -inf < ... < -0 < +0 < ... < +inf <
+ *    +NaN); equal scores compare by id as an unsigned 32-bit value, lowest
+ *    first (for the ids the merge produces, which are >= 0, this is the lowest
+ *    global token id); candidates that agree on score bits and id are ordered
+ *    by their position in the row, lowest first.
+ *  - Outputs list the selected candidates in candidate-position order.  When a
+ *    row has fewer than K candidates, slots [C, K) hold the padding candidate
+ *    (-inf, INT32_MAX), the same value that marks an empty shard slot.
+ *  - Every pointer to candidates, scores, ids or row starts is a DEVICE pointer
+ *    owned by the caller; host arrays of device pointers are read during the
+ *    call only.  The library allocates nothing, keeps no pointer and no global
+ *    state, and synchronises nothing: every call only enqueues work on
+ *    `stream`, so calls are safe from several host threads on several streams
+ *    and can be captured into a HIP graph.
+ *  - Errors are returned as negative status codes and never abort.  Arguments
+ *    are checked before anything is enqueued; a failed check enqueues nothing.
+ *    Faults inside a kernel surface at the caller's next synchronisation, as
+ *    with any asynchronous launch.
+ */
+#ifndef LIBDCPTOPK_H
+#define LIBDCPTOPK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Symbols of the C ABI; everything else in the library is hidden. */
+#define DCP_TOPK_API __attribute__((visibility("default")))
+
+/* Rows per step of the chunked merge (vLLM PR #59367, Purpose: the merge walks
+ * the rows 1024 at a time so its scratch stays bounded). */
+#define DCP_TOPK_MERGE_ROWS 1024
+
+/* Largest candidate count per row that dcp_topk_select accepts.  The pages
+ * benchmark rows of 4096, 8192 and 16384 candidates (PR #47348, Benchmarks). */
+#define DCP_TOPK_MAX_CANDIDATES 16384
+
+/* Alignment the chunked merge requires of its workspace, in bytes. */
+#define DCP_TOPK_WORKSPACE_ALIGN 256
+
+/* One packed candidate: fp32 score then int32 global token id, 8 bytes
+ * (PR #59367, Purpose: the packed candidates are a (T, K, 2) 32-bit array). */
+typedef struct dcp_topk_cand {
+  float score;
+  int32_t id;
+} dcp_topk_cand;
+
+/* Status codes. */
+enum {
+  DCP_TOPK_OK = 0,
+  DCP_TOPK_EINVAL = -1,       /* bad argument: null pointer, negative size,
+                                 k < 1, misaligned or overlapping buffers */
+  DCP_TOPK_EUNSUPPORTED = -2, /* valid but unsupported shape (num_cand above
+                                 DCP_TOPK_MAX_CANDIDATES); the caller can fall
+                                 back to another selector */
+  DCP_TOPK_EWORKSPACE = -3,   /* workspace too small or not 256-byte aligned */
+  DCP_TOPK_EHIP = -4          /* the HIP runtime rejected a launch */
+};
+
+/*
+ * dcp_topk_pack — one rank's local top-K into packed global candidates.
+ *
+ * PR #59367, Purpose: the pack step takes a row start per query row.  For row
+ * t in [0, rows) and slot j in [0, local_k):
+ *
+ *   dst[t * dst_row_stride + j] =
+ *       local_idx[t*src_row_stride + j] < 0
+ *         ? (-inf, INT32_MAX)                                   (invalid slot)
+ *         : (local_scores[t*src_row_stride + j],
+ *            local_idx[t*src_row_stride + j] + row_starts[t] + rank_offset)
+ *
+ * The id sum wraps in two's complement; the score is copied bit for bit.
+ *
+ *   local_scores    device, fp32, rows x local_k with row stride src_row_stride
+ *   local_idx       device, int32, same layout as local_scores
+ *   src_row_stride  elements between consecutive rows, >= local_k
+ *   row_starts      device, int32[rows]
+ *   rank_offset     added to every valid id of this rank
+ *   dst             device, 8-byte aligned; the first slot of this rank in
+ *                   row 0 of a row-major gathered buffer (for DCP rank r of a
+ *                   (rows, dcp*local_k) buffer: buffer + r*local_k)
+ *   dst_row_stride  candidates between consecutive rows of dst, >= local_k
+ *
+ * rows == 0 or local_k == 0 returns DCP_TOPK_OK and enqueues nothing.  The
+ * output must not overlap the inputs (DCP_TOPK_EINVAL).
+ */
+DCP_TOPK_API int dcp_topk_pack(const float* local_scores, const int32_t* local_idx, int64_t src_row_stride,
+                  const int32_t* row_starts, int32_t rank_offset, int32_t rows, int32_t local_k,
+                  dcp_topk_cand* dst, int64_t dst_row_stride, hipStream_t stream);
+
+/*
+ * dcp_topk_select — stable top-K of every row of a gathered candidate buffer.
+ *
+ * PR #47348, Summary: the selector radix-selects the K-th score key over the
+ * 32-bit score keys first and runs a token-id tie-break pass only when that
+ * threshold ties; the result equals ordering every candidate by the 64-bit key
+ * (score key in the high word, complemented id in the low word).
+ *
+ *   cand      device, 8-byte aligned, rows x num_cand candidates, row-major
+ *             (rank r's candidates of a row at columns [r*local_k, (r+1)*local_k)
+ *             when the buffer is a DCP gather; any order works)
+ *   rows      query rows, >= 0
+ *   num_cand  candidates per row, 0 <= num_cand <= DCP_TOPK_MAX_CANDIDATES
+ *   k         candidates to select per row, >= 1 (k > num_cand pads)
+ *   out       device, 8-byte aligned, rows x k candidates, row-major; must not
+ *             overlap cand
+ *
+ * Row t of out holds the min(k, num_cand) best candidates of row t of cand in
+ * candidate-position order, then padding.  rows == 0 returns DCP_TOPK_OK and
+ * enqueues nothing; cand may be NULL when num_cand == 0.
+ */
+DCP_TOPK_API int dcp_topk_select(const dcp_topk_cand* cand, int32_t rows, int32_t num_cand, int32_t k,
+                    dcp_topk_cand* out, hipStream_t stream);
+
+/*
+ * dcp_topk_merge_workspace_bytes — workspace that dcp_topk_merge_chunked needs:
+ * one chunk's row-major gathered buffer, min(rows, DCP_TOPK_MERGE_ROWS) * dcp *
+ * local_k * 8 bytes.  (PR #59367, Purpose, bounds the scratch of its
+ * multi-GPU merge at (1 + 2 dcp) * 8 * 1024 * K bytes; on one GPU nothing is
+ * exchanged, so only the buffer the selector reads remains.)  Returns 0 for
+ * negative arguments.
+ */
+DCP_TOPK_API size_t dcp_topk_merge_workspace_bytes(int32_t rows, int32_t dcp, int32_t local_k);
+
+/*
+ * dcp_topk_merge_chunked — the whole merge for one GPU: pack every rank's
+ * local top-K into the workspace and select, DCP_TOPK_MERGE_ROWS rows at a
+ * time (PR #59367, Purpose: the selector is row-independent, so walking the
+ * rows in chunks does not change the result).
+ *
+ *   local_scores  HOST array of dcp DEVICE pointers; rank r's fp32 scores,
+ *                 rows x local_k, contiguous rows
+ *   local_idx     HOST array of dcp DEVICE pointers; int32, same layout
+ *   row_starts    HOST array of dcp DEVICE pointers; int32[rows] each
+ *   rank_offsets  HOST array of dcp int32 values
+ *   dcp           ranks, >= 1; dcp * local_k <= DCP_TOPK_MAX_CANDIDATES
+ *   rows, local_k, k   as in dcp_topk_pack / dcp_topk_select
+ *   workspace     device, DCP_TOPK_WORKSPACE_ALIGN-aligned, at least
+ *                 dcp_topk_merge_workspace_bytes(rows, dcp, local_k) bytes;
+ *                 its contents on return are unspecified; it must not overlap
+ *                 any input or out
+ *   out           device, rows x k candidates; must not overlap any input
+ *
+ * Equivalent to dcp_topk_pack of every rank into a (rows, dcp*local_k) buffer
+ * followed by dcp_topk_select(buffer, rows, dcp*local_k, k, out).
+ */
+DCP_TOPK_API int dcp_topk_merge_chunked(const float* const* local_scores, const int32_t* const* local_idx,
+                           const int32_t* const* row_starts, const int32_t* rank_offsets, int32_t dcp,
+                           int32_t rows, int32_t local_k, int32_t k, void* workspace,
+                           size_t workspace_bytes, dcp_topk_cand* out, hipStream_t stream);
+
+/* Static, human-readable name of a status code. */
+DCP_TOPK_API const char* dcp_topk_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBDCPTOPK_H */

@@ -1,0 +1,172 @@
+// C ABI of libdcptopk: argument checks, launch dispatch and the chunked merge.
+//
+// Every check runs before anything is enqueued; no entry point allocates,
+// synchronises or keeps state.
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime.h>
+
+#include "internal.h"
+#include "libdcptopk.h"
+
+namespace {
+
+constexpr size_t kCandBytes = sizeof(dcp_topk_cand);
+static_assert(sizeof(dcp_topk_cand) == 8, "packed candidate is 8 bytes");
+
+struct Span {
+  uintptr_t begin;
+  uintptr_t bytes;
+};
+
+bool overlap(Span a, Span b) {
+  return a.bytes > 0 && b.bytes > 0 && a.begin < b.begin + b.bytes && b.begin < a.begin + a.bytes;
+}
+
+bool aligned(const void* p, uintptr_t a) { return reinterpret_cast<uintptr_t>(p) % a == 0; }
+
+// Bytes covered by `rows` rows of `width` elements of `elem` bytes at `stride`
+// elements per row; false on overflow.
+bool strided_span(const void* p, int64_t rows, int64_t width, int64_t stride, size_t elem, Span* out) {
+  if (rows <= 0 || width <= 0) {
+    *out = {reinterpret_cast<uintptr_t>(p), 0};
+    return true;
+  }
+  const unsigned __int128 n = static_cast<unsigned __int128>(rows - 1) * static_cast<uint64_t>(stride) +
+                              static_cast<uint64_t>(width);
+  const unsigned __int128 b = n * elem;
+  if (b > (static_cast<unsigned __int128>(1) << 62)) return false;
+  *out = {reinterpret_cast<uintptr_t>(p), static_cast<uintptr_t>(b)};
+  return true;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? DCP_TOPK_OK : DCP_TOPK_EHIP; }
+
+int check_select(const dcp_topk_cand* cand, int32_t rows, int32_t num_cand, int32_t k, const dcp_topk_cand* out) {
+  if (rows < 0 || num_cand < 0 || k < 1) return DCP_TOPK_EINVAL;
+  if (rows == 0) return DCP_TOPK_OK;
+  if (out == nullptr || (num_cand > 0 && cand == nullptr)) return DCP_TOPK_EINVAL;
+  if (!aligned(out, kCandBytes) || (cand != nullptr && !aligned(cand, kCandBytes))) return DCP_TOPK_EINVAL;
+  if (num_cand > DCP_TOPK_MAX_CANDIDATES) return DCP_TOPK_EUNSUPPORTED;
+  Span in_span, out_span;
+  if (!strided_span(cand, rows, num_cand, num_cand, kCandBytes, &in_span)) return DCP_TOPK_EINVAL;
+  if (!strided_span(out, rows, k, k, kCandBytes, &out_span)) return DCP_TOPK_EINVAL;
+  if (overlap(in_span, out_span)) return DCP_TOPK_EINVAL;
+  return DCP_TOPK_OK;
+}
+
+int check_pack(const float* scores, const int32_t* idx, int64_t src_row_stride, const int32_t* row_starts,
+               int32_t rows, int32_t local_k, const dcp_topk_cand* dst, int64_t dst_row_stride) {
+  if (rows < 0 || local_k < 0) return DCP_TOPK_EINVAL;
+  if (rows == 0 || local_k == 0) return DCP_TOPK_OK;
+  if (scores == nullptr || idx == nullptr || row_starts == nullptr || dst == nullptr) return DCP_TOPK_EINVAL;
+  if (src_row_stride < local_k || dst_row_stride < local_k) return DCP_TOPK_EINVAL;
+  if (!aligned(scores, 4) || !aligned(idx, 4) || !aligned(row_starts, 4) || !aligned(dst, kCandBytes))
+    return DCP_TOPK_EINVAL;
+  Span s, i, r, d;
+  if (!strided_span(scores, rows, local_k, src_row_stride, 4, &s) ||
+      !strided_span(idx, rows, local_k, src_row_stride, 4, &i) || !strided_span(row_starts, rows, 1, 1, 4, &r) ||
+      !strided_span(dst, rows, local_k, dst_row_stride, kCandBytes, &d))
+    return DCP_TOPK_EINVAL;
+  if (overlap(d, s) || overlap(d, i) || overlap(d, r)) return DCP_TOPK_EINVAL;
+  return DCP_TOPK_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* dcp_topk_status_string(int status) {
+  switch (status) {
+    case DCP_TOPK_OK:
+      return "ok";
+    case DCP_TOPK_EINVAL:
+      return "invalid argument";
+    case DCP_TOPK_EUNSUPPORTED:
+      return "unsupported shape";
+    case DCP_TOPK_EWORKSPACE:
+      return "workspace too small or misaligned";
+    case DCP_TOPK_EHIP:
+      return "HIP launch failed";
+    default:
+      return "unknown status";
+  }
+}
+
+size_t dcp_topk_merge_workspace_bytes(int32_t rows, int32_t dcp, int32_t local_k) {
+  if (rows < 0 || dcp < 0 || local_k < 0) return 0;
+  const int64_t chunk = rows < DCP_TOPK_MERGE_ROWS ? rows : DCP_TOPK_MERGE_ROWS;
+  return static_cast<size_t>(chunk) * static_cast<size_t>(dcp) * static_cast<size_t>(local_k) * kCandBytes;
+}
+
+int dcp_topk_select(const dcp_topk_cand* cand, int32_t rows, int32_t num_cand, int32_t k, dcp_topk_cand* out,
+                    hipStream_t stream) {
+  const int st = check_select(cand, rows, num_cand, k, out);
+  if (st != DCP_TOPK_OK || rows == 0) return st;
+  return hip_status(dcptopk::launch_select(cand, rows, num_cand, k, out, stream));
+}
+
+int dcp_topk_pack(const float* local_scores, const int32_t* local_idx, int64_t src_row_stride,
+                  const int32_t* row_starts, int32_t rank_offset, int32_t rows, int32_t local_k, dcp_topk_cand* dst,
+                  int64_t dst_row_stride, hipStream_t stream) {
+  const int st = check_pack(local_scores, local_idx, src_row_stride, row_starts, rows, local_k, dst, dst_row_stride);
+  if (st != DCP_TOPK_OK || rows == 0 || local_k == 0) return st;
+  const dcptopk::PackRank r{local_scores, local_idx, row_starts, rank_offset};
+  return hip_status(dcptopk::launch_pack(&r, 1, src_row_stride, rows, local_k, dst, dst_row_stride, stream));
+}
+
+int dcp_topk_merge_chunked(const float* const* local_scores, const int32_t* const* local_idx,
+                           const int32_t* const* row_starts, const int32_t* rank_offsets, int32_t dcp, int32_t rows,
+                           int32_t local_k, int32_t k, void* workspace, size_t workspace_bytes, dcp_topk_cand* out,
+                           hipStream_t stream) {
+  if (dcp < 1 || rows < 0 || local_k < 0 || k < 1) return DCP_TOPK_EINVAL;
+  if (local_scores == nullptr || local_idx == nullptr || row_starts == nullptr || rank_offsets == nullptr)
+    return DCP_TOPK_EINVAL;
+  if (static_cast<int64_t>(dcp) * local_k > DCP_TOPK_MAX_CANDIDATES) return DCP_TOPK_EUNSUPPORTED;
+  if (rows == 0) return DCP_TOPK_OK;
+  const int32_t num_cand = dcp * local_k;
+  const size_t need = dcp_topk_merge_workspace_bytes(rows, dcp, local_k);
+  if (need > 0 && (workspace == nullptr || !aligned(workspace, DCP_TOPK_WORKSPACE_ALIGN))) return DCP_TOPK_EWORKSPACE;
+  if (workspace_bytes < need) return DCP_TOPK_EWORKSPACE;
+  if (out == nullptr || !aligned(out, kCandBytes)) return DCP_TOPK_EINVAL;
+  Span ws{reinterpret_cast<uintptr_t>(workspace), need};
+  Span o;
+  if (!strided_span(out, rows, k, k, kCandBytes, &o)) return DCP_TOPK_EINVAL;
+  if (overlap(ws, o)) return DCP_TOPK_EINVAL;
+  for (int r = 0; r < dcp; ++r) {
+    const int st = check_pack(local_scores[r], local_idx[r], local_k, row_starts[r], rows, local_k,
+                              reinterpret_cast<const dcp_topk_cand*>(workspace), num_cand);
+    if (st != DCP_TOPK_OK) return st;
+    if (local_k == 0) continue;
+    Span s, i, rs;
+    strided_span(local_scores[r], rows, local_k, local_k, 4, &s);
+    strided_span(local_idx[r], rows, local_k, local_k, 4, &i);
+    strided_span(row_starts[r], rows, 1, 1, 4, &rs);
+    if (overlap(o, s) || overlap(o, i) || overlap(o, rs) || overlap(ws, s) || overlap(ws, i) || overlap(ws, rs))
+      return DCP_TOPK_EINVAL;
+  }
+
+  dcp_topk_cand* buf = static_cast<dcp_topk_cand*>(workspace);
+  for (int64_t c0 = 0; c0 < rows; c0 += DCP_TOPK_MERGE_ROWS) {
+    const int32_t n = static_cast<int32_t>(rows - c0 < DCP_TOPK_MERGE_ROWS ? rows - c0 : DCP_TOPK_MERGE_ROWS);
+    if (local_k > 0) {
+      for (int g = 0; g < dcp; g += dcptopk::kMaxPackRanks) {
+        const int nr = dcp - g < dcptopk::kMaxPackRanks ? dcp - g : dcptopk::kMaxPackRanks;
+        dcptopk::PackRank pr[dcptopk::kMaxPackRanks];
+        for (int r = 0; r < nr; ++r) {
+          pr[r] = {local_scores[g + r] + c0 * local_k, local_idx[g + r] + c0 * local_k, row_starts[g + r] + c0,
+                   rank_offsets[g + r]};
+        }
+        const hipError_t e = dcptopk::launch_pack(pr, nr, local_k, n, local_k, buf + static_cast<int64_t>(g) * local_k,
+                                                  num_cand, stream);
+        if (e != hipSuccess) return DCP_TOPK_EHIP;
+      }
+    }
+    const hipError_t e = dcptopk::launch_select(buf, n, num_cand, k, out + c0 * k, stream);
+    if (e != hipSuccess) return DCP_TOPK_EHIP;
+  }
+  return DCP_TOPK_OK;
+}
+
+}  // extern "C"

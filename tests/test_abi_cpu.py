@@ -1,0 +1,101 @@
+"""The C-ABI library on the CPU: it loads, exports every function the header
+declares, and its host-side checks return the documented status codes without
+enqueueing anything (no GPU is touched: every call here fails validation, or
+has rows == 0, before any HIP call)."""
+import ctypes
+import subprocess
+
+import pytest
+
+from oracle import stable_topk as O
+from stable_top_selection_amd import binding as B
+from stable_top_selection_amd.build import LIB_PATH
+
+P = ctypes.c_void_p
+DEV_A = 0x7F0000000000  # fake, 256-byte aligned device addresses: never dereferenced
+DEV_B = 0x7F0010000000
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return B.load_library()
+
+
+def test_exports_every_header_function(lib):
+    names = B.header_functions()
+    assert set(names) == {"dcp_topk_pack", "dcp_topk_select", "dcp_topk_merge_workspace_bytes",
+                          "dcp_topk_merge_chunked", "dcp_topk_status_string"}
+    for n in names:
+        assert hasattr(lib, n), n
+    exported = subprocess.run(["nm", "-D", "--defined-only", LIB_PATH], capture_output=True, text=True).stdout
+    public = sorted(line.split()[-1] for line in exported.splitlines() if " T dcp_topk_" in line)
+    assert public == names
+
+
+def test_status_strings(lib):
+    assert B.status_string(0) == "ok"
+    assert "invalid" in B.status_string(-1)
+    assert "unsupported" in B.status_string(-2)
+    assert "workspace" in B.status_string(-3)
+    assert "HIP" in B.status_string(-4)
+    assert B.status_string(99) == "unknown status"
+
+
+@pytest.mark.parametrize("rows,dcp,local_k", [(0, 4, 2048), (1, 4, 2048), (1024, 4, 2048), (1025, 4, 2048),
+                                              (8192, 4, 2048), (5, 3, 7), (-1, 4, 2048)])
+def test_workspace_bytes_match_oracle(lib, rows, dcp, local_k):
+    want = O.merge_workspace_bytes(rows, dcp, local_k) if rows >= 0 else 0
+    assert lib.dcp_topk_merge_workspace_bytes(rows, dcp, local_k) == want
+
+
+def test_select_argument_checks(lib):
+    s = lib.dcp_topk_select
+    assert s(None, 0, 8192, 2048, None, None) == B.OK  # no rows: nothing to do
+    assert s(None, 1, 8192, 2048, P(DEV_B), None) == B.EINVAL  # null input
+    assert s(P(DEV_A), 1, 8192, 2048, None, None) == B.EINVAL  # null output
+    assert s(P(DEV_A), 1, 8192, 0, P(DEV_B), None) == B.EINVAL  # k < 1
+    assert s(P(DEV_A), -1, 8192, 1, P(DEV_B), None) == B.EINVAL
+    assert s(P(DEV_A), 1, -5, 1, P(DEV_B), None) == B.EINVAL
+    assert s(P(DEV_A + 4), 1, 64, 1, P(DEV_B), None) == B.EINVAL  # misaligned input
+    assert s(P(DEV_A), 1, 64, 1, P(DEV_B + 2), None) == B.EINVAL  # misaligned output
+    assert s(P(DEV_A), 1, 16385, 1, P(DEV_B), None) == B.EUNSUPPORTED
+    # output overlapping the input: row 1 of the input is the output
+    assert s(P(DEV_A), 4, 64, 16, P(DEV_A + 64 * 8), None) == B.EINVAL
+
+
+def test_pack_argument_checks(lib):
+    p = lib.dcp_topk_pack
+    a, b, c, d = P(DEV_A), P(DEV_A + 0x100000), P(DEV_A + 0x200000), P(DEV_B)
+    assert p(None, None, 0, None, 0, 0, 16, None, 0, None) == B.OK  # no rows
+    assert p(a, b, 16, c, 0, 4, 0, d, 16, None) == B.OK  # no columns
+    assert p(None, b, 16, c, 0, 4, 16, d, 16, None) == B.EINVAL
+    assert p(a, b, 15, c, 0, 4, 16, d, 16, None) == B.EINVAL  # source stride < local_k
+    assert p(a, b, 16, c, 0, 4, 16, d, 15, None) == B.EINVAL  # dst stride < local_k
+    assert p(a, b, 16, c, 0, 4, 16, P(DEV_B + 4), 16, None) == B.EINVAL  # dst misaligned
+    assert p(a, b, 16, c, 0, 4, 16, b, 16, None) == B.EINVAL  # dst overlaps the indices
+    assert p(a, b, 16, c, 0, -4, 16, d, 16, None) == B.EINVAL
+
+
+def test_merge_argument_checks(lib):
+    m = lib.dcp_topk_merge_chunked
+    arr = ctypes.c_void_p * 2
+    sc = arr(DEV_A, DEV_A + 0x1000000)
+    ix = arr(DEV_A + 0x2000000, DEV_A + 0x3000000)
+    rs = arr(DEV_A + 0x4000000, DEV_A + 0x5000000)
+    offs = (ctypes.c_int32 * 2)(0, 1000)
+    ws_need = lib.dcp_topk_merge_workspace_bytes(64, 2, 128)
+    cast = lambda x: ctypes.cast(x, P)  # noqa: E731
+    args = lambda ws, wsb, out, dcp=2, rows=64, lk=128, k=64: (  # noqa: E731
+        cast(sc), cast(ix), cast(rs), cast(offs), dcp, rows, lk, k, P(ws), wsb, P(out), None)
+    assert m(*args(DEV_B, ws_need, DEV_B + 0x1000000, rows=0)) == B.OK
+    assert m(*args(DEV_B, ws_need, DEV_B + 0x1000000, dcp=0)) == B.EINVAL
+    assert m(*args(DEV_B, ws_need, DEV_B + 0x1000000, k=0)) == B.EINVAL
+    assert m(*args(DEV_B, ws_need, DEV_B + 0x1000000, lk=16384)) == B.EUNSUPPORTED
+    assert m(*args(DEV_B, ws_need - 1, DEV_B + 0x1000000)) == B.EWORKSPACE
+    assert m(*args(DEV_B + 64, ws_need, DEV_B + 0x1000000)) == B.EWORKSPACE  # not 256-byte aligned
+    assert m(*args(None, ws_need, DEV_B + 0x1000000)) == B.EWORKSPACE
+    assert m(*args(DEV_B, ws_need, DEV_B + 256)) == B.EINVAL  # out overlaps the workspace
+    assert m(*args(DEV_B, ws_need, DEV_A + 0x2000000)) == B.EINVAL  # out overlaps rank 0's indices
+    assert m(*args(DEV_A + 0x4000000, ws_need, DEV_B)) == B.EINVAL  # workspace overlaps row starts
+    assert m(None, cast(ix), cast(rs), cast(offs), 2, 64, 128, 64, P(DEV_B), ws_need, P(DEV_B + 0x1000000),
+             None) == B.EINVAL

@@ -1,0 +1,127 @@
+"""GPU parity of dcp_topk_pack and dcp_topk_merge_chunked with the CPU oracle."""
+import numpy as np
+import pytest
+import torch
+
+from gpu_helpers import DEV, to_dev
+from oracle import stable_topk as O
+from stable_top_selection_amd import binding as B
+from stable_top_selection_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+INT32_MAX = 2**31 - 1
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    B.load_library()
+
+
+def _shards_to_dev(sh):
+    return ([to_dev(sh.scores[r]) for r in range(sh.dcp)], [to_dev(sh.local_idx[r]) for r in range(sh.dcp)],
+            [to_dev(sh.row_starts[r]) for r in range(sh.dcp)], [int(x) for x in sh.rank_offsets])
+
+
+def _random_shards(rows, dcp, local_k, seed, invalid_frac=0.0, span=4096):
+    rng = np.random.default_rng(seed)
+    scores = rng.standard_normal((dcp, rows, local_k), dtype=np.float32)
+    if local_k <= span:
+        idx = np.stack([W.distinct_per_row(rng, rows, local_k, span) for _ in range(dcp)])
+    else:
+        idx = rng.integers(0, span, size=(dcp, rows, local_k), dtype=np.int32)
+    if invalid_frac:
+        idx = np.where(rng.random(idx.shape) < invalid_frac, np.int32(-1), idx).astype(np.int32)
+    starts = rng.integers(0, 131072, size=(dcp, rows), dtype=np.int32)
+    offs = (np.arange(dcp) * (131072 + span)).astype(np.int32)
+    return W.LocalShards("random", scores, idx, starts, offs, k=0)
+
+
+@pytest.mark.parametrize("rows,local_k,column,width", [(7, 2048, 2048, 8192), (5, 37, 3, 100), (3, 1, 0, 1),
+                                                      (1024, 2048, 0, 2048), (9, 1030, 0, 1030)])
+def test_pack_parity(rows, local_k, column, width):
+    sh = _random_shards(rows, 1, local_k, seed=rows + local_k, invalid_frac=0.05)
+    dst = torch.full((rows, width, 2), 123, dtype=torch.int32, device=DEV)
+    B.pack(to_dev(sh.scores[0]), to_dev(sh.local_idx[0]), to_dev(sh.row_starts[0]), 777, dst, column=column)
+    torch.cuda.synchronize()
+    want_s, want_i = O.pack(sh.scores[0], sh.local_idx[0], sh.row_starts[0], 777)
+    o = dst.cpu().numpy()
+    assert np.array_equal(o[:, column:column + local_k, 0].view(np.uint32), want_s.view(np.uint32))
+    assert np.array_equal(o[:, column:column + local_k, 1], want_i)
+    untouched = np.ones(width, bool)
+    untouched[column:column + local_k] = False
+    assert np.all(o[:, untouched] == 123), "pack wrote outside its columns"
+
+
+def test_pack_wraps_and_marks_invalid():
+    scores = torch.tensor([[1.5, -2.0, 3.0, 4.0]], dtype=torch.float32, device=DEV)
+    idx = torch.tensor([[2**31 - 10, -1, 0, -7]], dtype=torch.int32, device=DEV)
+    starts = torch.tensor([20], dtype=torch.int32, device=DEV)
+    dst = torch.zeros((1, 4, 2), dtype=torch.int32, device=DEV)
+    B.pack(scores, idx, starts, 5, dst)
+    o = dst.cpu().numpy()
+    want_s, want_i = O.pack(scores.cpu().numpy(), idx.cpu().numpy(), starts.cpu().numpy(), 5)
+    assert np.array_equal(o[..., 1], want_i) and np.array_equal(o[..., 0].view(np.uint32), want_s.view(np.uint32))
+    assert o[0, 1, 1] == INT32_MAX and o[0, 3, 1] == INT32_MAX
+
+
+def _merge_parity(sh, k, label):
+    sc, ix, rs, offs = _shards_to_dev(sh)
+    out = B.merge_chunked(sc, ix, rs, offs, k)
+    torch.cuda.synchronize()
+    want_s, want_i = O.merge(sh.scores, sh.local_idx, sh.row_starts, sh.rank_offsets, k)
+    o = out.cpu().numpy()
+    ok_rows = (o[..., 0].view(np.uint32) == want_s.view(np.uint32)).all(1) & (o[..., 1] == want_i).all(1)
+    assert ok_rows.all(), f"{label}: {np.count_nonzero(~ok_rows)} rows differ, first {np.nonzero(~ok_rows)[0][0]}"
+
+
+@pytest.mark.parametrize("rows", [1, 5, 1024, 1025, 2 * 1024 + 5])
+def test_merge_chunked_prefill_shape(rows):
+    """DCP 4 x local K 2048, K 2048, across chunk boundaries (2*1024+5 rows is
+    the row count of PR #59367's chunk-walk test)."""
+    sh = W.prefill(rows=rows, seed=50 + rows)
+    print(f"[merge parity] T={rows} digest={sh.digest()}", flush=True)
+    _merge_parity(sh, 2048, f"prefill T={rows}")
+
+
+def test_merge_chunked_full_prefill():
+    """The prefill workload at full size: T = 8192 rows in 8 chunks."""
+    sh = W.prefill()
+    print(f"[merge parity] {sh.name} digest={sh.digest()}", flush=True)
+    _merge_parity(sh, sh.k, sh.name)
+
+
+@pytest.mark.parametrize("rows,dcp,local_k,k", [(37, 3, 100, 50), (20, 9, 64, 100), (11, 2, 7, 20),
+                                               (1030, 4, 33, 1), (6, 16, 1024, 2048), (4, 4, 0, 3)])
+def test_merge_chunked_ragged(rows, dcp, local_k, k):
+    sh = _random_shards(rows, dcp, local_k, seed=rows * dcp + local_k, invalid_frac=0.1, span=max(local_k, 128))
+    _merge_parity(sh, k, f"ragged rows={rows} dcp={dcp} local_k={local_k} k={k}")
+
+
+def test_merge_equals_pack_then_select():
+    """The driver equals the two public calls composed on the caller's side."""
+    sh = W.prefill(rows=300, seed=9)
+    sc, ix, rs, offs = _shards_to_dev(sh)
+    gathered = torch.empty((300, 4 * 2048, 2), dtype=torch.int32, device=DEV)
+    for r in range(4):
+        B.pack(sc[r], ix[r], rs[r], offs[r], gathered, column=r * 2048)
+    a = B.select(gathered, 2048)
+    b = B.merge_chunked(sc, ix, rs, offs, 2048)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+def test_merge_workspace_errors():
+    sh = W.prefill(rows=8, seed=1, local_k=64)
+    sc, ix, rs, offs = _shards_to_dev(sh)
+    need = B.merge_workspace_bytes(8, 4, 64)
+    assert need == O.merge_workspace_bytes(8, 4, 64)
+    small = torch.empty(need - 8, dtype=torch.uint8, device=DEV)
+    with pytest.raises(B.DcpTopkError) as e:
+        B.merge_chunked(sc, ix, rs, offs, 16, workspace=small)
+    assert e.value.status == B.EWORKSPACE
+    big = torch.empty(need + 512, dtype=torch.uint8, device=DEV)
+    with pytest.raises(B.DcpTopkError) as e:  # 8 bytes past a 256-byte boundary
+        B.merge_chunked(sc, ix, rs, offs, 16, workspace=big[8:8 + need])
+    assert e.value.status == B.EWORKSPACE

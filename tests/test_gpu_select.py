@@ -1,0 +1,175 @@
+"""GPU parity of dcp_topk_select with the CPU oracle: bit-exact scores and ids.
+
+Covers the five workloads at full size, the decode rows sweep, ragged sizes on
+both load paths, the degenerate cases, heavy-tie trials, adversarial floats,
+determinism and guard bands around the output.
+"""
+import numpy as np
+import pytest
+import torch
+
+from gpu_helpers import DEV, assert_select_parity, gpu_select, to_dev
+from stable_top_selection_amd import binding as B
+from stable_top_selection_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    B.load_library()
+
+
+@pytest.mark.parametrize("name", ["tiny", "decode", "large", "tie_heavy"])
+def test_workloads_full_size(name):
+    g = getattr(W, name)()
+    print(f"[select parity] {g.name} rows={g.rows} C={g.num_cand} k={g.k} digest={g.digest()}", flush=True)
+    assert_select_parity(g.scores, g.ids, g.k, g.name, guard=2)
+
+
+@pytest.mark.parametrize("rows", [1, 8, 32, 64])
+def test_decode_rows_sweep(rows):
+    g = W.decode(rows)
+    assert_select_parity(g.scores, g.ids, g.k, g.name)
+
+
+RAGGED = [
+    # (rows, C, k, dist)
+    (3, 1, 1, "normal"), (3, 2, 1, "normal"), (5, 3, 2, "uniform"), (4, 63, 7, "normal"),
+    (4, 64, 63, "levels"), (4, 65, 64, "special"), (7, 255, 100, "normal"), (2, 256, 1, "uniform"),
+    (3, 1000, 999, "normal"), (3, 1023, 500, "levels"), (3, 1024, 1023, "normal"), (3, 1025, 1, "special"),
+    (5, 2047, 2046, "uniform"), (5, 2048, 2047, "normal"), (5, 2049, 1000, "levels"), (3, 3001, 1500, "const"),
+    (4, 4095, 2048, "normal"), (4, 4096, 2048, "uniform"), (4, 4097, 2048, "levels"), (3, 6000, 5999, "special"),
+    (3, 8191, 2048, "normal"), (3, 8193, 2048, "uniform"), (2, 12345, 4000, "levels"), (2, 16383, 2048, "normal"),
+    (2, 16384, 2048, "uniform"), (2, 16384, 16383, "levels"), (2, 16384, 1, "normal"),
+]
+
+
+@pytest.mark.parametrize("rows,c,k,dist", RAGGED)
+def test_ragged_sizes(rows, c, k, dist):
+    g = W.random_gathered(rows, c, k, seed=1000 + c + k, dist=dist)
+    assert_select_parity(g.scores, g.ids, k, g.name, guard=1)
+
+
+@pytest.mark.parametrize("rows,c,k", [(3, 4096, 2048), (3, 8192, 2048), (2, 1000, 10)])
+def test_eight_byte_load_path(rows, c, k):
+    """A candidate buffer that is 8- but not 16-byte aligned takes the 8-byte loads."""
+    g = W.random_gathered(rows, c, k, seed=77 + c, dist="normal")
+    assert_select_parity(g.scores, g.ids, k, g.name, misalign=True)
+
+
+@pytest.mark.parametrize("c,k", [(1, 1), (5, 9), (100, 100), (100, 2048), (8192, 8192), (8192, 9000)])
+def test_k_at_least_num_cand_copies_and_pads(c, k):
+    g = W.random_gathered(3, c, k, seed=c + k, dist="normal")
+    assert_select_parity(g.scores, g.ids, k, g.name, guard=1)
+
+
+def test_empty_rows_only_padding():
+    out = torch.full((4, 5, 2), 7, dtype=torch.int32, device=DEV)
+    B.select(torch.empty((4, 0, 2), dtype=torch.int32, device=DEV), 5, out=out)
+    o = out.cpu().numpy()
+    assert np.all(o[..., 0].view(np.uint32) == 0xFF800000) and np.all(o[..., 1] == 2**31 - 1)
+
+
+def test_zero_rows_is_a_no_op():
+    out = torch.empty((0, 4, 2), dtype=torch.int32, device=DEV)
+    B.select(torch.empty((0, 16, 2), dtype=torch.int32, device=DEV), 4, out=out)
+
+
+@pytest.mark.parametrize("dist,pad", [("levels", 0.3), ("const", 0.0), ("special", 0.5), ("normal", 0.9)])
+def test_padding_and_full_duplicates(dist, pad):
+    """Padding slots are identical (score, id) pairs; with repeated ids the
+    boundary cuts through identical candidates and position decides."""
+    g = W.random_gathered(8, 8192, 2048, seed=31, dist=dist, pad_frac=pad)
+    assert_select_parity(g.scores, g.ids, g.k, g.name)
+    g = W.random_gathered(8, 5000, 1234, seed=32, dist=dist, id_span=64, repeat_ids=True, pad_frac=pad)
+    assert_select_parity(g.scores, g.ids, g.k, g.name)
+
+
+def test_all_padding_and_all_tie_rows():
+    c, k = 8192, 2048
+    scores = np.full((4, c), -np.inf, np.float32)
+    ids = np.full((4, c), 2**31 - 1, np.int32)
+    scores[1] = 3.0
+    ids[1] = np.random.default_rng(5).permutation(c).astype(np.int32)
+    scores[2, :k] = 1.0  # exactly k real candidates, the rest padding
+    ids[2, :k] = np.arange(k, dtype=np.int32)[::-1]
+    scores[3, ::2] = 0.5  # every other slot real, ids all equal
+    ids[3, ::2] = 9
+    assert_select_parity(scores, ids, k, "all-padding / all-tie")
+
+
+def test_heavy_tie_trials():
+    """Many tie-heavy rows (every row ties at the threshold score), in the
+    spirit of the repeated heavy-tie trials on PR #47348's review: 3 x 256 rows."""
+    for seed in (11, 12, 13):
+        g = W.tie_heavy(rows=256, seed=seed)
+        assert_select_parity(g.scores, g.ids, g.k, f"tie_heavy seed {seed}")
+
+
+def test_adversarial_floats():
+    """NaNs of both signs and several payloads, +-0, +-inf, subnormals."""
+    rng = np.random.default_rng(8)
+    specials = np.array([0x7FC00000, 0xFFC00000, 0x7F800001, 0xFFFFFFFF, 0x7FFFFFFF, 0x80000000, 0x00000000,
+                         0x7F800000, 0xFF800000, 0x00000001, 0x80000001, 0x3F800000, 0xBF800000], np.uint32)
+    bits = rng.integers(0, 2**32, size=(16, 8192), dtype=np.uint64).astype(np.uint32)
+    mask = rng.random(bits.shape) < 0.5
+    bits = np.where(mask, specials[rng.integers(0, len(specials), size=bits.shape)], bits)
+    ids = rng.integers(0, 50, size=bits.shape).astype(np.int32)
+    for k in (1, 2048, 8191):
+        assert_select_parity(bits.view(np.float32), ids, k, f"adversarial k={k}")
+
+
+def test_negative_ids_compare_unsigned():
+    """Outside the merge's id range: ids compare as uint32 through ~id."""
+    scores = np.ones((2, 300), np.float32)
+    ids = np.random.default_rng(3).integers(-2**31, 2**31 - 1, size=(2, 300), dtype=np.int64).astype(np.int32)
+    assert_select_parity(scores, ids, 100, "negative ids")
+
+
+def test_deterministic_repeats():
+    g = W.tie_heavy(rows=64, seed=21)
+    first = gpu_select(g.scores, g.ids, g.k)
+    for _ in range(5):
+        again = gpu_select(g.scores, g.ids, g.k)
+        assert np.array_equal(first[0], again[0]) and np.array_equal(first[1], again[1])
+
+
+def test_unsupported_and_invalid_arguments():
+    cand = torch.zeros((2, 16385, 2), dtype=torch.int32, device=DEV)
+    with pytest.raises(B.DcpTopkError) as e:
+        B.select(cand, 10)
+    assert e.value.status == B.EUNSUPPORTED
+    cand = torch.zeros((2, 64, 2), dtype=torch.int32, device=DEV)
+    with pytest.raises(B.DcpTopkError) as e:  # output aliasing the input
+        B.select(cand, 64, out=cand)
+    assert e.value.status == B.EINVAL
+
+
+def test_graph_capture_replay_with_changing_inputs():
+    """The select is a pure enqueue: capture once, replay on new inputs."""
+    rows, c, k = 32, 8192, 2048
+    static_in = torch.empty((rows, c, 2), dtype=torch.int32, device=DEV)
+    static_out = torch.empty((rows, k, 2), dtype=torch.int32, device=DEV)
+    g0 = W.random_gathered(rows, c, k, seed=100)
+    static_in.copy_(to_dev(g0.interleaved()))
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        B.select(static_in, k, out=static_out)  # warm up outside the graph
+    torch.cuda.current_stream().wait_stream(s)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        B.select(static_in, k, out=static_out)
+    for seed in (101, 102, 103):
+        g = W.random_gathered(rows, c, k, seed=seed, dist="levels" if seed % 2 else "normal")
+        static_in.copy_(to_dev(g.interleaved()))
+        graph.replay()
+        torch.cuda.synchronize()
+        want_b, want_i = gpu_select(g.scores, g.ids, k)  # eager run between replays
+        o = static_out.cpu().numpy()
+        assert np.array_equal(o[..., 0].view(np.uint32), want_b) and np.array_equal(o[..., 1], want_i)
+        from oracle import stable_topk as O
+        ob, oi = O.select(g.scores, g.ids, k)
+        assert np.array_equal(want_b, ob.view(np.uint32)) and np.array_equal(want_i, oi)
