@@ -134,16 +134,19 @@ int dcp_topk_merge_chunked(const float* const* local_scores, const int32_t* cons
   Span o;
   if (!strided_span(out, rows, k, k, kCandBytes, &o)) return DCP_TOPK_EINVAL;
   if (overlap(ws, o)) return DCP_TOPK_EINVAL;
-  for (int r = 0; r < dcp; ++r) {
-    const int st = check_pack(local_scores[r], local_idx[r], local_k, row_starts[r], rows, local_k,
-                              reinterpret_cast<const dcp_topk_cand*>(workspace), num_cand);
-    if (st != DCP_TOPK_OK) return st;
-    if (local_k == 0) continue;
-    Span s, i, rs;
-    strided_span(local_scores[r], rows, local_k, local_k, 4, &s);
-    strided_span(local_idx[r], rows, local_k, local_k, 4, &i);
-    strided_span(row_starts[r], rows, 1, 1, 4, &rs);
-    if (overlap(o, s) || overlap(o, i) || overlap(o, rs) || overlap(ws, s) || overlap(ws, i) || overlap(ws, rs))
+  // The workspace holds one chunk (at most DCP_TOPK_MERGE_ROWS rows); the
+  // inputs span all rows.
+  for (int r = 0; r < dcp && local_k > 0; ++r) {
+    const float* sc = local_scores[r];
+    const int32_t* ix = local_idx[r];
+    const int32_t* rs = row_starts[r];
+    if (sc == nullptr || ix == nullptr || rs == nullptr) return DCP_TOPK_EINVAL;
+    if (!aligned(sc, 4) || !aligned(ix, 4) || !aligned(rs, 4)) return DCP_TOPK_EINVAL;
+    Span s, i, rsp;
+    if (!strided_span(sc, rows, local_k, local_k, 4, &s) || !strided_span(ix, rows, local_k, local_k, 4, &i) ||
+        !strided_span(rs, rows, 1, 1, 4, &rsp))
+      return DCP_TOPK_EINVAL;
+    if (overlap(o, s) || overlap(o, i) || overlap(o, rsp) || overlap(ws, s) || overlap(ws, i) || overlap(ws, rsp))
       return DCP_TOPK_EINVAL;
   }
 
