@@ -1,0 +1,405 @@
+#!/usr/bin/env python3
+"""Benchmark of the stable DCP top-K select on one MI355X.
+
+Headline (one JSON line on stdout): ``dcp_topk_select`` on the large workload,
+256 rows x 8192 candidates (DCP 4 x local K 2048), K 2048, scores U(-10,10).
+One step = one select launch over the whole batch.  Algorithmic bytes per
+launch = rows*C*8 read + rows*K*8 written = 20,971,520.
+
+Timing follows the pages' selector microbenchmark (PR #47348, Benchmarks:
+median over 7 trials of 200 launches, warm-up excluded).  The launches of a
+trial are captured once in a HIP graph and replayed, so the per-launch time is
+the GPU's and not the host's launch rate; HIP events on the replay stream
+bracket every trial.  Inputs rotate through a pool larger than twice the
+MI355X's Infinity Cache plus L2 (2 x (256 + 32) MiB), so every launch reads its
+candidates from HBM ("cold").  Warm-cache numbers (one buffer reused) are
+reported separately and labelled.
+
+Other lines of the same JSON object: the decode rows sweep and the tie-heavy
+workload as latencies, the chunked prefill merge (T = 8192) as a whole-driver
+time, the CPU oracle timed on the host (``cpu_baseline``), and the roofline of
+the select kernel.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "select µs/launch + candidates/s and % peak HBM BW (rows=256, 8192 cand, K=2048)"
+PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, AMD published peak
+MIB = 1 << 20
+COLD_POOL_BYTES = 2 * (256 + 32) * MIB  # 2 x (Infinity Cache + 8 x 4 MiB L2)
+CAND_BYTES = 8
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "select_large_rows256_traffic.json")
+SELECT_SOURCE = os.path.join(ROOT, "stable_top_selection_amd", "csrc", "select.hip")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse_args():
+    p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200, help="select launches per timed trial")
+    p.add_argument("--warmup", type=int, default=20, help="untimed launches before timing")
+    p.add_argument("--trials", type=int, default=7)
+    p.add_argument("--configs", default="large,large_warm,large_eager,decode,tie_heavy,prefill",
+                   help="comma list of large_warm, large_eager, decode, tie_heavy, prefill; the cold large "
+                        "headline always runs (--configs large runs it alone, as profiled)")
+    p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    p.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU oracle work to time")
+    p.add_argument("--pmc", action="store_true",
+                   help="counter-collection mode: a 512 MiB torch copy (calibration) then cold select launches, "
+                        "no timing and no JSON")
+    return p.parse_args()
+
+
+def select_bytes(rows, c, k):
+    return rows * c * CAND_BYTES + rows * k * CAND_BYTES
+
+
+class Runner:
+    """Raw C-ABI launches with precomputed pointers (no per-call Python checks)."""
+
+    def __init__(self):
+        import torch
+
+        from stable_top_selection_amd import binding as B
+
+        self.torch = torch
+        self.B = B
+        self.lib = B.load_library()
+        self.dev = torch.device("cuda:0")
+
+    def select(self, cand_ptr, rows, c, k, out_ptr, stream_ptr):
+        st = self.lib.dcp_topk_select(cand_ptr, rows, c, k, out_ptr, stream_ptr)
+        if st != 0:
+            raise RuntimeError(f"dcp_topk_select: {self.B.status_string(st)}")
+
+    def stream_ptr(self):
+        return self.torch.cuda.current_stream().cuda_stream
+
+    def graph_of(self, fns):
+        """Capture fns (each takes a stream pointer) into one HIP graph."""
+        torch = self.torch
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            fns[0](self.stream_ptr())  # first launch outside capture
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            sp = self.stream_ptr()
+            for f in fns:
+                f(sp)
+        return g
+
+    def time_graph(self, g, trials):
+        """Milliseconds of each replay, bracketed by events on the replay stream."""
+        torch = self.torch
+        g.replay()
+        torch.cuda.synchronize()
+        out = []
+        for _ in range(trials):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record()
+            g.replay()
+            e1.record()
+            e1.synchronize()
+            out.append(e0.elapsed_time(e1))
+        return out
+
+
+def make_pool(run, inter, k, pool_bytes):
+    """Copies of one input (rows, C, 2) int32 spread over >= pool_bytes, with
+    one output per copy.  Returns (list of (cand_ptr, out_ptr), tensors)."""
+    torch = run.torch
+    rows, c, _ = inter.shape
+    per = select_bytes(rows, c, k)
+    n = max(1, -(-pool_bytes // per))
+    src = torch.from_numpy(inter).to(run.dev)
+    cands = torch.empty((n, rows, c, 2), dtype=torch.int32, device=run.dev)
+    cands.copy_(src.unsqueeze(0).expand(n, rows, c, 2))
+    outs = torch.empty((n, rows, k, 2), dtype=torch.int32, device=run.dev)
+    ptrs = [(cands[i].data_ptr(), outs[i].data_ptr()) for i in range(n)]
+    return ptrs, (src, cands, outs)
+
+
+def check_pool_outputs(run, tensors, gathered, k, sample):
+    """Bit-exact check of sampled pool outputs against the CPU oracle."""
+    import numpy as np
+
+    from oracle import stable_topk as oracle
+
+    _, cands, outs = tensors
+    want_s, want_i = oracle.select(gathered.scores, gathered.ids, k)
+    idx = sorted(set([0, outs.shape[0] - 1] + list(range(0, outs.shape[0], max(1, outs.shape[0] // sample)))))
+    for i in idx:
+        o = outs[i].cpu().numpy()
+        if not (np.array_equal(o[..., 0].view(np.uint32), want_s.view(np.uint32)) and np.array_equal(o[..., 1], want_i)):
+            raise AssertionError(f"bench output {i} differs from the oracle ({gathered.name})")
+    return len(idx)
+
+
+def bench_select(run, g, steps, warmup, trials, cold=True):
+    """Median per-launch microseconds of a graph of launches rotating over a cold pool."""
+    inter = g.interleaved()
+    pool_bytes = COLD_POOL_BYTES if cold else 0
+    ptrs, tensors = make_pool(run, inter, g.k, pool_bytes)
+    n = len(ptrs)
+    launches = max(steps, n) if cold else steps
+    rows, c, k = g.rows, g.num_cand, g.k
+
+    def fn(i):
+        cp, op = ptrs[i % n]
+        return lambda sp: run.select(cp, rows, c, k, op, sp)
+
+    for i in range(warmup):
+        fn(i)(run.stream_ptr())
+    run.torch.cuda.synchronize()
+    graph = run.graph_of([fn(i) for i in range(launches)])
+    ms = run.time_graph(graph, trials)
+    checked = check_pool_outputs(run, tensors, g, k, sample=4)
+    us = [1e3 * m / launches for m in ms]
+    del graph, tensors
+    run.torch.cuda.empty_cache()
+    return {"us_per_launch": statistics.median(us), "us_trials": [round(x, 4) for x in us], "launches": launches,
+            "pool_buffers": n, "outputs_checked": checked}
+
+
+def bench_eager(run, g, steps, trials):
+    """Same launches without a graph (host launch rate included), cold pool."""
+    ptrs, tensors = make_pool(run, g.interleaved(), g.k, COLD_POOL_BYTES)
+    torch = run.torch
+    n = len(ptrs)
+    res = []
+    sp = run.stream_ptr()
+    for _ in range(trials):
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(steps):
+            cp, op = ptrs[i % n]
+            run.select(cp, g.rows, g.num_cand, g.k, op, sp)
+        e1.record()
+        e1.synchronize()
+        res.append(1e3 * e0.elapsed_time(e1) / steps)
+    del tensors
+    return statistics.median(res)
+
+
+def bench_prefill(run, trials):
+    """Whole chunked merge at T = 8192 (8 chunks of 1024 rows) in one graph, and
+    the select launches of the same chunks on their own."""
+    import ctypes
+
+    import numpy as np
+
+    from oracle import stable_topk as oracle
+    from stable_top_selection_amd import workloads as W
+
+    torch = run.torch
+    sh = W.prefill()
+    to = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(run.dev)  # noqa: E731
+    sc = [to(sh.scores[r]) for r in range(sh.dcp)]
+    ix = [to(sh.local_idx[r]) for r in range(sh.dcp)]
+    rs = [to(sh.row_starts[r]) for r in range(sh.dcp)]
+    offs = [int(x) for x in sh.rank_offsets]
+    T, dcp, lk, k = sh.rows, sh.dcp, sh.local_k, sh.k
+    need = run.B.merge_workspace_bytes(T, dcp, lk)
+    ws = torch.empty(need, dtype=torch.uint8, device=run.dev)
+    out = torch.empty((T, k, 2), dtype=torch.int32, device=run.dev)
+    arr = ctypes.c_void_p * dcp
+    sp_, ip_, rp_ = arr(*[t.data_ptr() for t in sc]), arr(*[t.data_ptr() for t in ix]), arr(*[t.data_ptr() for t in rs])
+    of_ = (ctypes.c_int32 * dcp)(*offs)
+    cast = lambda x: ctypes.cast(x, ctypes.c_void_p)  # noqa: E731
+
+    def merge(stream_ptr):
+        st = run.lib.dcp_topk_merge_chunked(cast(sp_), cast(ip_), cast(rp_), cast(of_), dcp, T, lk, k,
+                                            ws.data_ptr(), need, out.data_ptr(), stream_ptr)
+        if st != 0:
+            raise RuntimeError(run.B.status_string(st))
+
+    graph = run.graph_of([merge])
+    ms = run.time_graph(graph, trials)
+    # sampled rows against the oracle (the oracle on all 8192 rows takes ~10 s)
+    rows = np.unique(np.concatenate([np.arange(0, T, 97), [1023, 1024, 4095, 4096, T - 1]]))
+    want_s, want_i = oracle.merge(sh.scores[:, rows], sh.local_idx[:, rows], sh.row_starts[:, rows], sh.rank_offsets, k)
+    o = out.cpu().numpy()[rows]
+    if not (np.array_equal(o[..., 0].view(np.uint32), want_s.view(np.uint32)) and np.array_equal(o[..., 1], want_i)):
+        raise AssertionError("prefill merge differs from the oracle on sampled rows")
+    # select alone on the 8 chunk-sized gathered buffers the merge builds
+    gathered = ws.view(torch.int32).view(min(T, 1024), dcp * lk, 2)
+    chunk_outs = [out[c0:c0 + 1024] for c0 in range(0, T, 1024)]
+    sel = [lambda spp, o_=o_: run.select(gathered.data_ptr(), 1024, dcp * lk, k, o_.data_ptr(), spp)
+           for o_ in chunk_outs]
+    g2 = run.graph_of(sel)
+    ms_sel = run.time_graph(g2, trials)
+    merge_ms = statistics.median(ms)
+    sel_ms = statistics.median(ms_sel)
+    sel_bytes = 8 * select_bytes(1024, dcp * lk, k)
+    pack_bytes = 8 * dcp * 1024 * lk * (4 + 4 + 8) + dcp * T * 4
+    return {"workload": f"prefill chunked: T={T}, DCP {dcp} x local K {lk}, K {k}, 1024-row chunks",
+            "merge_ms": round(merge_ms, 4), "merge_trials_ms": [round(x, 4) for x in ms],
+            "select_only_ms": round(sel_ms, 4), "pack_ms_by_difference": round(merge_ms - sel_ms, 4),
+            "merge_GBps": round((sel_bytes + pack_bytes) / (merge_ms * 1e-3) / 1e9, 1),
+            "select_GBps_L2_warm_workspace": round(sel_bytes / (sel_ms * 1e-3) / 1e9, 1),
+            "rows_checked": int(len(rows))}
+
+
+def cpu_baseline(g, seconds):
+    """The CPU oracle (numpy, single-threaded sort) on the same workload."""
+    from oracle import stable_topk as oracle
+
+    times = []
+    t_end = time.perf_counter() + seconds
+    while len(times) < 3 or time.perf_counter() < t_end:
+        t0 = time.perf_counter()
+        oracle.select(g.scores, g.ids, g.k)
+        times.append(time.perf_counter() - t0)
+    t = statistics.median(times)
+    return {"value": g.rows * g.num_cand / t, "unit": "candidates/s", "cores": 1, "kind": "oracle",
+            "sample": f"the full {g.name} batch ({g.rows} x {g.num_cand}, K {g.k}) through the numpy oracle, "
+                      f"{len(times)} runs in {sum(times):.1f} s, median {t * 1e3:.1f} ms per batch",
+            "host_cpus_visible": len(os.sched_getaffinity(0))}
+
+
+def traffic_record(launch_us):
+    """HBM traffic per launch from the committed counter summary, only if it
+    was taken on the select kernel source as it is now."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    with open(TRAFFIC_FILE) as f:
+        rec = json.load(f)
+    with open(SELECT_SOURCE, "rb") as f:
+        digest = hashlib.sha256(f.read()).hexdigest()
+    if rec.get("select_source_sha256") != digest:
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def pmc_mode(run):
+    """Fixed short sequence for rocprofv3 --pmc: a known-size copy, then cold selects."""
+    from stable_top_selection_amd import workloads as W
+
+    torch = run.torch
+    n = 512 * MIB // 4
+    a = torch.ones(n, dtype=torch.int32, device=run.dev)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    g = W.large()
+    ptrs, tensors = make_pool(run, g.interleaved(), g.k, COLD_POOL_BYTES)
+    sp = run.stream_ptr()
+    for i in range(64):
+        cp, op = ptrs[i % len(ptrs)]
+        run.select(cp, g.rows, g.num_cand, g.k, op, sp)
+    torch.cuda.synchronize()
+    log(f"pmc mode: 3 copies of {512} MiB, then 64 cold select launches ({len(ptrs)} pool buffers)")
+
+
+def main():
+    args = parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: the select path is not sharded across GPUs "
+              "(each DCP rank runs the same select on its own gathered buffer); run with --gpus 1",
+              file=sys.stderr)
+        sys.exit(2)
+    from stable_top_selection_amd import workloads as W
+
+    run = Runner()
+    if args.pmc:
+        pmc_mode(run)
+        return
+    configs = [c.strip() for c in args.configs.split(",") if c.strip()]
+    props = run.torch.cuda.get_device_properties(run.dev)
+    log(f"device: {props.name} ({getattr(props, 'gcnArchName', '?')}), {props.multi_processor_count} CUs")
+
+    g = W.large()
+    log(f"[large] rows={g.rows} C={g.num_cand} k={g.k} digest={g.digest()}")
+    res = bench_select(run, g, args.steps, args.warmup, args.trials, cold=True)
+    us = res["us_per_launch"]
+    per_launch_bytes = select_bytes(g.rows, g.num_cand, g.k)
+    gbs = per_launch_bytes / (us * 1e-6) / 1e9
+    log(f"[large] cold {us:.3f} us/launch, {gbs:.0f} GB/s ({100 * gbs / PEAK_HBM_GBS:.1f}% of peak)")
+    extra = {"large_cold": res}
+    if "large_warm" in configs:
+        warm = bench_select(run, g, args.steps, args.warmup, args.trials, cold=False)
+        extra["large_warm_L2_MALL_not_HBM"] = warm
+        log(f"[large] warm (one buffer, cache-resident) {warm['us_per_launch']:.3f} us/launch")
+    if "large_eager" in configs:
+        eager = bench_eager(run, g, args.steps, args.trials)
+        extra["large_eager_cold_us_per_launch"] = round(eager, 4)
+        log(f"[large] eager launches (host launch rate included) {eager:.3f} us/launch")
+    if "decode" in configs:
+        sweep = {}
+        for rows in (1, 8, 16, 32, 64):
+            gd = W.decode(rows)
+            cold = bench_select(run, gd, args.steps, args.warmup, args.trials, cold=True)
+            hot = bench_select(run, gd, args.steps, args.warmup, args.trials, cold=False)
+            sweep[f"rows{rows}"] = {"cold_us": round(cold["us_per_launch"], 3), "warm_us": round(hot["us_per_launch"], 3)}
+            log(f"[decode rows={rows}] cold {cold['us_per_launch']:.3f} us, warm {hot['us_per_launch']:.3f} us")
+        extra["decode_latency_us"] = sweep
+    if "tie_heavy" in configs:
+        gt = W.tie_heavy()
+        cold = bench_select(run, gt, args.steps, args.warmup, args.trials, cold=True)
+        hot = bench_select(run, gt, args.steps, args.warmup, args.trials, cold=False)
+        extra["tie_heavy_latency_us"] = {"rows": gt.rows, "cold_us": round(cold["us_per_launch"], 3),
+                                         "warm_us": round(hot["us_per_launch"], 3)}
+        log(f"[tie_heavy] cold {cold['us_per_launch']:.3f} us, warm {hot['us_per_launch']:.3f} us")
+    if "prefill" in configs:
+        extra["prefill"] = bench_prefill(run, args.trials)
+        log(f"[prefill] {extra['prefill']}")
+
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline(g, args.cpu_seconds)
+        log(f"[cpu oracle] {cpu['value']:.3e} candidates/s ({cpu['sample']})")
+
+    traffic = traffic_record(us)
+    line = {
+        "metric": METRIC,
+        "value": g.rows * g.num_cand / (us * 1e-6),
+        "unit": "candidates/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": us * 1e-3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "u32",
+        "data": "synthetic",
+        "config": {"workload": "large: 256 rows x 8192 candidates (DCP 4 x local K 2048), K 2048, scores U(-10,10), "
+                               "inputs rotated through a 576+ MiB pool (HBM-cold)",
+                   "rows": g.rows, "num_cand": g.num_cand, "k": g.k},
+        "us_per_launch": us,
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": traffic,
+                     "kernel": "stable_topk_select_kernel<2,4>", "algorithmic_bytes_per_launch": per_launch_bytes},
+        "cpu_baseline": cpu,
+        "context": {"pages_selector_us_rows256_c8192": 15.459,
+                    "pages_note": "PR #47348 Benchmarks, median of 7x200 launches; hardware and K not stated"},
+        "extra": extra,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
