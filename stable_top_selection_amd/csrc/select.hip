@@ -4,34 +4,43 @@
 // selector finds the K-th best 32-bit score key by radix selection instead of
 // sorting 64-bit (score key, complemented id) keys, and runs a token-id
 // tie-break pass only when that score threshold ties.  The review comment on
-// the same page describes the race this design avoids: the threshold was
-// broadcast through shared memory that was then cleared for the next phase
-// with no barrier in between, so late waves read a zero threshold and lost
-// every tied candidate.  Here every pass broadcasts through its own LDS slot,
-// histograms alternate between two buffers, and a buffer is cleared only after
-// the barrier that ends its last read.
+// the same page describes a race to avoid: a threshold broadcast through shared
+// memory that is cleared for the next phase without a barrier in between, so
+// that late waves read a cleared threshold and drop every tied candidate.  This
+// kernel has no broadcast slot at all: every wave scans the histogram itself
+// and reaches the same digit, and histogram buffers rotate through three, so a
+// buffer is cleared only one full barrier after its last read and refilled one
+// barrier after that.
 //
-// One workgroup of 1024 threads (16 wave64s) owns one row.  Thread t keeps the
-// candidates at positions v*VEC*1024 + VEC*t + j (v < NV, j < VEC) in VGPRs
-// for the whole kernel, so the row is read from HBM exactly once; with VEC = 2
-// every wave reads 1 KiB of contiguous candidates per 16-byte load.
+// One workgroup (256 or 512 threads: 4 or 8 wave64s) owns one row.  Every
+// thread keeps N candidates in VGPRs for the whole kernel, at positions
+// v*VEC*BLOCK + VEC*t + j (chunk v < N/VEC, j < VEC), so the row is read from
+// HBM once, with 16-byte loads when VEC = 2 (each wave reads 1 KiB of
+// consecutive candidates per load instruction).
 //
 // Per row:
-//   1. score key  key = bits ^ (negative ? 0xFFFFFFFF : 0x80000000), an
-//      order-preserving uint32 (IEEE totalOrder).
-//   2. radix select on the key, MSB first, digits of 11, 11 and 10 bits.  Each
-//      pass histograms the digit of the candidates that still match the prefix
-//      (LDS atomics), then a suffix scan over the bins (DPP wave scan plus one
-//      cross-wave step) finds the digit holding the K-th best key.  When the
-//      chosen bin holds exactly the candidates still needed, the remaining
-//      passes are skipped.
-//   3. only if more candidates share the threshold key than are still needed:
-//      the same radix select on u = ~id among the tied candidates (largest u =
-//      lowest id first).  If even (key, id) ties at the boundary, candidate
-//      position decides (lowest first).
-//   4. stable compaction: selected flags -> wave ballots -> mbcnt prefix ->
-//      one cross-wave scan in (chunk, wave, lane) order, which is candidate
-//      position order -> each selected candidate is stored at its rank.
+//   1. key = bits ^ (negative ? 0xFFFFFFFF : 0x80000000), an order-preserving
+//      uint32 of the fp32 score (IEEE totalOrder).
+//   2. Pass 0: LDS-atomic histogram of the top 11 key bits over the whole row.
+//      Each atomic returns the item's rank inside its bin.  Every wave then
+//      finds the bin d0 holding the K-th best key (two-level suffix scan: DPP
+//      wave scans and ballots).
+//   3. The items of bin d0 (a few percent of the row for smooth scores) write
+//      themselves into an LDS list at their rank.  The remaining 21 key bits
+//      are radix-selected over the list only (digits of 8, 8, 5 bits, small
+//      histograms), stopping as soon as the chosen bin holds exactly the items
+//      still needed.  A bin too large for the list falls back to the same
+//      passes over the register-resident row (digits of 11 and 10 bits).
+//   4. Only if more items share the threshold key than are still needed: the
+//      same radix selection on u = ~id over the tied items (largest u = lowest
+//      id).  If identical (key, id) pairs still straddle the boundary, the
+//      lowest positions win.
+//   5. Stable compaction: per-chunk selected counts packed 4 to a word, scanned
+//      across the wave with DPP and across waves through LDS (one barrier) in
+//      (chunk, wave, lane) order = candidate-position order.  Every item then
+//      issues one raw buffer store at its rank; unselected items store to an
+//      offset past the buffer's range, which the hardware drops, so the loop
+//      has no per-item branch.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -40,19 +49,14 @@
 namespace dcptopk {
 namespace {
 
-constexpr int kBlock = 1024;
 constexpr int kWave = 64;
-constexpr int kWaves = kBlock / kWave;
-constexpr int kBins = 2048;       // widest digit: 11 bits
-constexpr int kMaxPasses = 6;     // 3 score passes + 3 id passes
-constexpr int kMaxSegments = 16 * kWaves;  // (chunk, wave) pairs, chunks <= 16
+constexpr int kBins = 2048;      // widest digit: 11 bits
+constexpr int kSmallBins = 256;  // list passes: digits of at most 8 bits
+constexpr int kListCap = 2048;   // largest threshold bucket handled as a list
+constexpr uint32_t kBufferWord3 = 0x00020000u;  // raw buffer resource, gfx9 family
+constexpr uint32_t kDropOffset = 0x80000000u;   // beyond any num_records used here
 
-struct alignas(16) SelectLds {
-  uint32_t hist[2][kBins];            // digit histograms, alternating by pass
-  uint32_t wave_total[2][kWaves];     // cross-wave step of the bin scan
-  uint32_t slot[kMaxPasses][4];       // per-pass broadcast: digit, above, count
-  uint32_t segment[2][kMaxSegments];  // per (chunk, wave) flag counts
-};
+typedef int int2v __attribute__((ext_vector_type(2)));
 
 // LDS-only workgroup barrier: waits for this wave's LDS traffic, not for its
 // outstanding global loads, so the row's loads stay in flight across it.
@@ -62,12 +66,18 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+__device__ __forceinline__ uint32_t lane_of(uint32_t x, int lane) {
+  return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(x), lane));
+}
+
+__device__ __forceinline__ int first_lane(uint64_t ballot) { return __builtin_ctzll(ballot); }
+
 __device__ __forceinline__ uint32_t uniform(uint32_t x) {
   return static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(x)));
 }
 
-__device__ __forceinline__ uint32_t lane_of(uint32_t x, int lane) {
-  return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(x), lane));
+__device__ __forceinline__ uint32_t lds_add(uint32_t* p) {
+  return __hip_atomic_fetch_add(p, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
 
 // Inclusive prefix sum across the 64 lanes of a wave: Hillis-Steele inside
@@ -85,81 +95,93 @@ __device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t v, int lane) {
   return v;
 }
 
-// Number of set bits of a wave ballot in lanes below this one.
-__device__ __forceinline__ uint32_t ballot_below(uint64_t b) {
-  return __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(b >> 32),
-                                   __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(b), 0u));
-}
-
 __device__ __forceinline__ uint32_t score_key(uint32_t bits) {
   return bits ^ (static_cast<uint32_t>(static_cast<int32_t>(bits) >> 31) | 0x80000000u);
 }
 
-__device__ __forceinline__ uint32_t key_to_bits(uint32_t key) {
-  return key ^ (static_cast<uint32_t>(static_cast<int32_t>(~key) >> 31) | 0x80000000u);
-}
-
 struct Digit {
-  uint32_t digit;  // bin holding the K-th best value among the matching ones
-  uint32_t above;  // matching values in higher bins
-  uint32_t count;  // matching values in that bin
+  uint32_t digit;  // bin holding the need-th largest value among those counted
+  uint32_t above;  // counted values in higher bins
+  uint32_t count;  // counted values in that bin
 };
 
-// Suffix scan of an NB-bin histogram: returns the bin d with
-// above(d) < need <= above(d) + hist[d], where above(d) counts higher bins.
-// Requires 1 <= need <= total.  Thread t reads the NB/1024 bins just below
-// NB - (NB/1024)*t, so thread order is descending bin order.
+// Finds the bin d of an NB-bin histogram (NB >= 256) with above(d) < need <=
+// above(d) + hist[d], where above(d) sums the bins above d.  Every wave runs
+// this on its own and gets the same (wave-uniform) answer.  Requires
+// 1 <= need <= total.
+//
+// Level 1: lane l sums the PER bins [NB - PER*(l+1), NB - PER*l), so lane
+// order is descending bin order; a wave scan and a ballot give the first lane
+// whose running count reaches `need`.  Level 2: that lane's PER bins, one per
+// lane, highest first; a second scan and ballot give the bin.
 template <int NB>
-__device__ __forceinline__ Digit find_digit(const uint32_t* hist, uint32_t need, uint32_t* wave_total,
-                                            uint32_t* slot, int t, int lane, int w) {
-  constexpr int kPer = NB / kBlock;
-  static_assert(kPer == 1 || kPer == 2, "1024 or 2048 bins");
-  const int lo = NB - kPer * (t + 1);
-  uint32_t h[kPer];  // h[0] is this thread's highest bin
-  if constexpr (kPer == 2) {
-    const uint2 x = *reinterpret_cast<const uint2*>(hist + lo);
-    h[0] = x.y;
-    h[1] = x.x;
-  } else {
-    h[0] = hist[lo];
-  }
+__device__ __forceinline__ Digit find_digit(const uint32_t* hist, uint32_t need, int lane) {
+  constexpr int PER = NB / kWave;
+  constexpr int VECS = PER / 4;
+  static_assert(VECS >= 1, "at least 256 bins");
+  const uint4* p = reinterpret_cast<const uint4*>(hist + NB - PER * (lane + 1));
   uint32_t sum = 0;
 #pragma unroll
-  for (int i = 0; i < kPer; ++i) sum += h[i];
-  const uint32_t incl = wave_inclusive_scan(sum, lane);
-  if (lane == kWave - 1) wave_total[w] = incl;
-  lds_barrier();
-  uint32_t before = 0;
-#pragma unroll
-  for (int i = 0; i < kWaves; ++i) before += (i < w) ? wave_total[i] : 0u;
-  uint32_t above = before + incl - sum;
-#pragma unroll
-  for (int i = 0; i < kPer; ++i) {
-    if (above < need && need <= above + h[i]) {
-      slot[0] = static_cast<uint32_t>(lo + kPer - 1 - i);
-      slot[1] = above;
-      slot[2] = h[i];
-    }
-    above += h[i];
+  for (int i = 0; i < VECS; ++i) {
+    // rotate the start by lane so that the 64 lanes' 16-byte reads spread over
+    // all banks instead of all starting on the same one
+    const uint4 x = p[(i + lane) & (VECS - 1)];
+    sum += x.x + x.y + x.z + x.w;
   }
-  lds_barrier();
+  const uint32_t incl = wave_inclusive_scan(sum, lane);
+  const int L = first_lane(__ballot(incl >= need));
+  const uint32_t above_l = lane_of(incl, L) - lane_of(sum, L);
+  const int top = NB - PER * L - 1;  // highest bin of lane L
+  const uint32_t h = lane < PER ? hist[top - lane] : 0u;
+  const uint32_t incl2 = wave_inclusive_scan(h, lane);
+  const int i = first_lane(__ballot(lane < PER && above_l + incl2 >= need));
   Digit d;
-  d.digit = uniform(slot[0]);
-  d.above = uniform(slot[1]);
-  d.count = uniform(slot[2]);
+  d.digit = static_cast<uint32_t>(top - i);
+  d.count = lane_of(h, i);
+  d.above = above_l + lane_of(incl2, i) - d.count;
   return d;
 }
 
-// Clear the bins find_digit<NB> read in this thread.
+// The same search for the small histograms of the list passes (NB <= 256):
+// lane l holds PER = max(1, NB/64) bins; the bin inside lane L is resolved in
+// scalar registers.
 template <int NB>
-__device__ __forceinline__ void clear_bins(uint32_t* hist, int t) {
-  constexpr int kPer = NB / kBlock;
-  const int lo = NB - kPer * (t + 1);
-  if constexpr (kPer == 2) {
-    *reinterpret_cast<uint2*>(hist + lo) = make_uint2(0u, 0u);
+__device__ __forceinline__ Digit find_digit_small(const uint32_t* hist, uint32_t need, int lane) {
+  constexpr int PER = NB >= kWave ? NB / kWave : 1;
+  constexpr int LANES = NB / PER;
+  static_assert(PER == 1 || PER == 2 || PER == 4, "1, 2 or 4 bins per lane");
+  uint32_t h[PER];  // h[0] = this lane's highest bin
+  const int lo = NB - PER * (lane + 1);
+  if constexpr (PER == 4) {
+    const uint4 x = *reinterpret_cast<const uint4*>(hist + lo);
+    h[0] = x.w;
+    h[1] = x.z;
+    h[2] = x.y;
+    h[3] = x.x;
   } else {
-    hist[lo] = 0u;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) h[j] = lane < LANES ? hist[lo + PER - 1 - j] : 0u;
   }
+  uint32_t sum = 0;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) sum += h[j];
+  const uint32_t incl = wave_inclusive_scan(sum, lane);
+  const int L = first_lane(__ballot(lane < LANES && incl >= need));
+  uint32_t above = lane_of(incl, L) - lane_of(sum, L);
+  Digit d{0u, 0u, 0u};
+  bool found = false;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const uint32_t c = lane_of(h[j], L);
+    if (!found && above + c >= need) {
+      d.digit = static_cast<uint32_t>(NB - PER * L - 1 - j);
+      d.above = above;
+      d.count = c;
+      found = true;
+    }
+    above += c;
+  }
+  return d;
 }
 
 // Radix-select state of one value stream (score keys, or complemented ids).
@@ -170,230 +192,401 @@ struct Radix {
   uint32_t count;   // values matching prefix after the last pass
 };
 
-// One MSB-first pass over the digit at SHIFT (BITS wide) of the eligible
-// values that match the prefix.
-template <int SHIFT, int BITS, int N>
-__device__ __forceinline__ void radix_pass(SelectLds& lds, int pass, const uint32_t (&val)[N], uint32_t eligible,
-                                           Radix& st, int t, int lane, int w) {
-  constexpr int NB = 1 << BITS;
-  constexpr uint32_t kDigitMask = NB - 1;
-  uint32_t* hist = lds.hist[pass & 1];
-#pragma unroll
-  for (int i = 0; i < N; ++i) {
-    if (((eligible >> i) & 1u) && (val[i] & st.mask) == st.prefix) {
-      __hip_atomic_fetch_add(hist + ((val[i] >> SHIFT) & kDigitMask), 1u, __ATOMIC_RELAXED,
-                             __HIP_MEMORY_SCOPE_WORKGROUP);
-    }
-  }
-  lds_barrier();
-  const Digit d = find_digit<NB>(hist, st.need, lds.wave_total[pass & 1], lds.slot[pass], t, lane, w);
-  clear_bins<NB>(hist, t);  // reused two passes later, after at least one barrier
-  st.prefix |= d.digit << SHIFT;
-  st.mask |= kDigitMask << SHIFT;
+__device__ __forceinline__ void advance(Radix& st, const Digit& d, int shift, uint32_t digit_mask) {
+  st.prefix |= d.digit << shift;
+  st.mask |= digit_mask << shift;
   st.need -= d.above;
   st.count = d.count;
 }
 
-// Up to three passes (11, 11, 10 bits); stops early once the chosen bin holds
-// exactly the values still needed.  Returns the number of passes run.
-template <int N>
-__device__ __forceinline__ int radix_select(SelectLds& lds, int pass, const uint32_t (&val)[N], uint32_t eligible,
-                                            Radix& st, int t, int lane, int w) {
-  radix_pass<21, 11>(lds, pass, val, eligible, st, t, lane, w);
-  if (st.count == st.need) return 1;
-  radix_pass<10, 11>(lds, pass + 1, val, eligible, st, t, lane, w);
-  if (st.count == st.need) return 2;
-  radix_pass<0, 10>(lds, pass + 2, val, eligible, st, t, lane, w);
-  return 3;
+template <int BLOCK>
+struct alignas(16) SelectLds {
+  static constexpr int kWaves = BLOCK / kWave;
+  uint32_t hist[3][kBins];         // pass 0 (hist[0]) and the register passes, rotating
+  uint32_t small[3][kSmallBins];   // list passes, rotating
+  uint2 list[kListCap];            // (key, id) of the items in the pass-0 threshold bin
+  uint32_t segment[2][kWaves];     // per-wave flagged counts (dup scan, select scan)
+  uint32_t sink[kWave];            // per-lane target of atomics whose item does not count
+  uint32_t common[8];              // OR / AND of list keys and ids, per wave pair
+};
+
+// Clear `words` (a multiple of 4) words of LDS.
+template <int BLOCK>
+__device__ __forceinline__ void clear_words(uint32_t* p, int words, int t) {
+  for (int i = 4 * t; i < words; i += 4 * BLOCK) *reinterpret_cast<uint4*>(p + i) = make_uint4(0u, 0u, 0u, 0u);
 }
 
-// Exclusive prefix count of `flags` (bit i = item i) in candidate-position
-// order (chunk v, thread t, slot j).  Needs one barrier; `segment` must not be
-// read by any other phase between the two barriers around this call.
-template <int VEC, int NV>
-__device__ __forceinline__ void position_scan(uint32_t flags, uint32_t* segment, uint32_t (&rank)[VEC * NV],
-                                              int lane, int w) {
-  constexpr int kEntries = NV * kWaves;
-  constexpr int kPerLane = (kEntries + kWave - 1) / kWave;
-  uint32_t below[NV];
+// Register pass p >= 1 over the digit at SHIFT (BITS wide) of the eligible
+// values that match the prefix.  Uses hist[p % 3]; after its barrier clears
+// hist[(p + 2) % 3], which pass p - 1 used and pass p + 2 will use.
+template <int BLOCK, int SHIFT, int BITS, int N>
+__device__ __forceinline__ void radix_pass(SelectLds<BLOCK>& lds, int pass, const uint32_t (&val)[N],
+                                           uint32_t eligible, Radix& st, int t, int lane) {
+  constexpr int NB = 1 << BITS;
+  constexpr uint32_t kDigitMask = NB - 1;
+  uint32_t* hist = lds.hist[pass % 3];
+  uint32_t* sink = lds.sink + lane;
+  // every item issues its atomic, to its bin if it counts, else to this lane's
+  // sink word: no per-item branch
 #pragma unroll
-  for (int v = 0; v < NV; ++v) {
-    uint32_t before = 0, total = 0;
-#pragma unroll
-    for (int j = 0; j < VEC; ++j) {
-      const uint64_t b = __ballot((flags >> (v * VEC + j)) & 1u);
-      before += ballot_below(b);
-      total += static_cast<uint32_t>(__popcll(b));
-    }
-    below[v] = before;
-    if (lane == 0) segment[v * kWaves + w] = total;
+  for (int i = 0; i < N; ++i) {
+    const bool counts = ((eligible >> i) & 1u) && (val[i] & st.mask) == st.prefix;
+    lds_add(counts ? hist + ((val[i] >> SHIFT) & kDigitMask) : sink);
   }
   lds_barrier();
-  // every wave scans all (chunk, wave) totals itself: no second barrier
-  uint32_t x[kPerLane];
-  uint32_t sum = 0;
-#pragma unroll
-  for (int e = 0; e < kPerLane; ++e) {
-    const int idx = lane * kPerLane + e;
-    x[e] = idx < kEntries ? segment[idx] : 0u;
-    sum += x[e];
+  clear_words<BLOCK>(lds.hist[(pass + 2) % 3], kBins, t);
+  advance(st, find_digit<NB>(hist, st.need, lane), SHIFT, kDigitMask);
+}
+
+// List pass q over the digit at SHIFT (BITS wide): score keys of the list
+// (BY_ID false) or complemented ids of the list items whose key is `thr`.
+// Uses small[q % 3]; after its barrier clears small[(q + 2) % 3], which pass
+// q - 1 used and pass q + 2 will use.  Pass 0 of the score keys is counted
+// while the list is built, so this starts at pass 1.
+template <int BLOCK, int SHIFT, int BITS, bool BY_ID>
+__device__ __forceinline__ void list_pass(SelectLds<BLOCK>& lds, int q, int m, uint32_t thr, Radix& st, int t,
+                                          int lane) {
+  constexpr int NB = 1 << BITS;
+  constexpr uint32_t kDigitMask = NB - 1;
+  uint32_t* hist = lds.small[q % 3];
+  for (int e = t; e < m; e += BLOCK) {
+    const uint2 x = lds.list[e];
+    const uint32_t v = BY_ID ? ~x.y : x.x;
+    if ((!BY_ID || x.x == thr) && (v & st.mask) == st.prefix) lds_add(hist + ((v >> SHIFT) & kDigitMask));
   }
-  const uint32_t incl = wave_inclusive_scan(sum, lane);
-  uint32_t ex[kPerLane];
-  ex[0] = incl - sum;
+  lds_barrier();
+  if (t < kSmallBins / 4) *reinterpret_cast<uint4*>(lds.small[(q + 2) % 3] + 4 * t) = make_uint4(0u, 0u, 0u, 0u);
+  advance(st, find_digit_small<NB>(hist, st.need, lane), SHIFT, kDigitMask);
+}
+
+// OR and AND of the list's keys and complemented ids over the whole
+// workgroup (bits where every list item agrees: ~(or ^ and)).  One barrier.
+template <int BLOCK>
+__device__ __forceinline__ void list_common_bits(SelectLds<BLOCK>& lds, int m, int t, int lane, int w, uint32_t& kor,
+                                                 uint32_t& kand, uint32_t& uor, uint32_t& uand) {
+  uint32_t a = 0u, b = ~0u, c = 0u, d = ~0u;
+  for (int e = t; e < m; e += BLOCK) {
+    const uint2 x = lds.list[e];
+    a |= x.x;
+    b &= x.x;
+    c |= ~x.y;
+    d &= ~x.y;
+  }
+  // fold across the wave, then across waves through LDS atomics
 #pragma unroll
-  for (int e = 1; e < kPerLane; ++e) ex[e] = ex[e - 1] + x[e - 1];
+  for (int s = 1; s < kWave; s <<= 1) {
+    a |= __shfl_xor(a, s);
+    b &= __shfl_xor(b, s);
+    c |= __shfl_xor(c, s);
+    d &= __shfl_xor(d, s);
+  }
+  if (w == 0 && lane < 8) lds.common[lane] = (lane & 1) ? ~0u : 0u;  // or-slots 0, and-slots ~0
+  lds_barrier();
+  if (lane == 0) {
+    __hip_atomic_fetch_or(lds.common + 0, a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    __hip_atomic_fetch_and(lds.common + 1, b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    __hip_atomic_fetch_or(lds.common + 2, c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    __hip_atomic_fetch_and(lds.common + 3, d, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  }
+  lds_barrier();
+  kor = uniform(lds.common[0]);
+  kand = uniform(lds.common[1]);
+  uor = uniform(lds.common[2]);
+  uand = uniform(lds.common[3]);
+}
+
+// Exclusive rank of every flagged item (flag[i] is 0 or 1) among all flagged
+// items of the row in candidate-position order.  Wave w owns the contiguous
+// positions [w*64*N, (w+1)*64*N); inside it, chunk v holds 64*VEC consecutive
+// positions, lane-major.  So a rank is: flagged items of earlier waves (one
+// number per wave, exchanged through LDS: one barrier) + of earlier chunks of
+// this wave (scalar) + of earlier lanes in this chunk (packed DPP scan) + of
+// earlier slots of this thread.  `segment` must belong to this call alone.
+template <int BLOCK, int VEC, int N>
+__device__ __forceinline__ void position_rank(const uint32_t (&flag)[N], uint32_t* segment, uint32_t (&rank)[N],
+                                              int lane, int w) {
+  constexpr int NV = N / VEC;       // chunks per thread
+  constexpr int NW = (NV + 3) / 4;  // packed words: 4 chunk counts of 8 bits each
+  constexpr int kWaves = BLOCK / kWave;
+  // per-thread count of flagged items in each chunk (<= VEC), packed; a wave's
+  // running count of one chunk is <= 64*VEC <= 128, so fields never carry
+  uint32_t packed[NW];
+#pragma unroll
+  for (int q = 0; q < NW; ++q) packed[q] = 0;
 #pragma unroll
   for (int v = 0; v < NV; ++v) {
-    const int entry = v * kWaves + w;
-    uint32_t base = 0;
+    uint32_t c = 0;
 #pragma unroll
-    for (int e = 0; e < kPerLane; ++e) {
-      const uint32_t b = lane_of(ex[e], entry / kPerLane);
-      base = (entry % kPerLane == e) ? b : base;
-    }
-    uint32_t own = 0;
+    for (int j = 0; j < VEC; ++j) c += flag[v * VEC + j];
+    packed[v / 4] += c << (8 * (v % 4));
+  }
+  uint32_t excl[NW], total[NW];
+#pragma unroll
+  for (int q = 0; q < NW; ++q) {
+    const uint32_t incl = wave_inclusive_scan(packed[q], lane);
+    excl[q] = incl - packed[q];
+    total[q] = lane_of(incl, kWave - 1);  // this wave's count of each chunk, packed
+  }
+  uint32_t chunk_base[NV];  // flagged items of this wave before chunk v (scalar)
+  uint32_t wave_total = 0;
+#pragma unroll
+  for (int v = 0; v < NV; ++v) {
+    chunk_base[v] = wave_total;
+    wave_total += (total[v / 4] >> (8 * (v % 4))) & 0xFFu;
+  }
+  if (lane == 0) segment[w] = wave_total;
+  lds_barrier();
+  uint32_t before = 0;
+#pragma unroll
+  for (int i = 0; i < kWaves; ++i) before += i < w ? segment[i] : 0u;
+  before = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(before)));
+#pragma unroll
+  for (int v = 0; v < NV; ++v) {
+    uint32_t own = before + chunk_base[v] + ((excl[v / 4] >> (8 * (v % 4))) & 0xFFu);
 #pragma unroll
     for (int j = 0; j < VEC; ++j) {
-      rank[v * VEC + j] = base + below[v] + own;
-      own += (flags >> (v * VEC + j)) & 1u;
+      rank[v * VEC + j] = own;
+      own += flag[v * VEC + j];
     }
   }
 }
 
-template <int VEC, int NV>
-__global__ __launch_bounds__(kBlock) void stable_topk_select_kernel(const dcp_topk_cand* __restrict__ cand,
-                                                                    int32_t num_cand, int32_t k,
-                                                                    dcp_topk_cand* __restrict__ out) {
-  constexpr int N = VEC * NV;
-  static_assert(N <= 32, "flags are 32-bit masks");
-  static_assert(NV * kWaves <= kMaxSegments, "segment table");
-  __shared__ SelectLds lds;
+template <int BLOCK, int VEC, int N, bool FULL>
+__global__ __launch_bounds__(BLOCK) void stable_topk_select_kernel(const dcp_topk_cand* __restrict__ cand,
+                                                                   int32_t num_cand, int32_t k,
+                                                                   dcp_topk_cand* __restrict__ out) {
+  static_assert(N <= 32 && N % VEC == 0, "flags are 32-bit masks");
+  constexpr int NV = N / VEC;
+  constexpr int kChunk = VEC * kWave;  // consecutive positions per chunk and wave
+  __shared__ SelectLds<BLOCK> lds;
 
   const int t = threadIdx.x;
   const int lane = t & (kWave - 1);
-  const int w = static_cast<int>(uniform(static_cast<uint32_t>(t >> 6)));
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6);
   const int64_t row = blockIdx.x;
   const int C = num_cand;
-  const uint32_t* in = reinterpret_cast<const uint32_t*>(cand + row * C);
+  const dcp_topk_cand* in = cand + row * C;
   uint2* o = reinterpret_cast<uint2*>(out + row * static_cast<int64_t>(k));
 
   // k >= C: every candidate is selected, in place, then padding
   if (k >= C) {
     const uint2* src = reinterpret_cast<const uint2*>(in);
-    for (int s = t; s < C; s += kBlock) o[s] = src[s];
+    for (int s = t; s < C; s += BLOCK) o[s] = src[s];
     const uint2 pad = make_uint2(0xFF800000u, 0x7FFFFFFFu);
-    for (int s = C + t; s < k; s += kBlock) o[s] = pad;
+    for (int s = C + t; s < k; s += BLOCK) o[s] = pad;
     return;
   }
 
-  // 1. issue every load of the row before touching LDS.  Here C > k >= 1, so
-  // clamping a position past the row to the last full vector keeps every
-  // load in bounds without a branch; such items are masked out by `valid`.
-  uint32_t key[N], idv[N];
-  uint32_t valid = 0;
+  // 1. issue every load of the row before touching LDS: raw buffer loads over
+  // the row (positions past C read as zero and are masked out by `valid`); the
+  // chunk offset is a scalar, so a load costs no vector instruction.  Wave w
+  // reads positions [w*64*N, (w+1)*64*N), 1 KiB (VEC = 2) per load instruction.
+  const __amdgpu_buffer_rsrc_t src = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<dcp_topk_cand*>(in), 0, C * static_cast<int>(sizeof(dcp_topk_cand)), static_cast<int>(kBufferWord3));
+  const int first = w * kWave * N + VEC * lane;  // this thread's position in chunk 0
+  const int voff = first * static_cast<int>(sizeof(dcp_topk_cand));
+  uint32_t bits[N], idv[N];
 #pragma unroll
   for (int v = 0; v < NV; ++v) {
-    const int q = v * VEC * kBlock + VEC * t;
-    const int qc = q < C ? q : C - VEC;
+    const int soff = v * kChunk * static_cast<int>(sizeof(dcp_topk_cand));
     if constexpr (VEC == 2) {
-      const uint4 x = *reinterpret_cast<const uint4*>(in + 2 * static_cast<int64_t>(qc));
-      key[2 * v] = x.x;
+      const int4 x = __builtin_bit_cast(int4, __builtin_amdgcn_raw_buffer_load_b128(src, voff, soff, 0));
+      bits[2 * v] = x.x;
       idv[2 * v] = x.y;
-      key[2 * v + 1] = x.z;
+      bits[2 * v + 1] = x.z;
       idv[2 * v + 1] = x.w;
-      if (q < C) valid |= 3u << (2 * v);  // C is even on this path
     } else {
-      const uint2 x = *reinterpret_cast<const uint2*>(in + 2 * static_cast<int64_t>(qc));
-      key[v] = x.x;
+      const int2v x = __builtin_amdgcn_raw_buffer_load_b64(src, voff, soff, 0);
+      bits[v] = x.x;
       idv[v] = x.y;
-      if (q < C) valid |= 1u << v;
     }
   }
+  // FULL: the row fills every slot (C == BLOCK*N); else the last are masked out
+  uint32_t valid = 0xFFFFFFFFu >> (32 - N);
+  if constexpr (!FULL) {
+    valid = 0;
+#pragma unroll
+    for (int v = 0; v < NV; ++v)
+#pragma unroll
+      for (int j = 0; j < VEC; ++j) valid |= (first + v * kChunk + j < C) ? 1u << (v * VEC + j) : 0u;
+  }
 
-  // clear both histogram buffers while the loads are in flight; the key
-  // transform stays after the barrier so that pass 1 starts on the first
-  // chunk while later chunks are still arriving
-  *reinterpret_cast<uint2*>(&lds.hist[0][2 * t]) = make_uint2(0u, 0u);
-  *reinterpret_cast<uint2*>(&lds.hist[1][2 * t]) = make_uint2(0u, 0u);
+  // clear the histograms while the loads are in flight; the key transform
+  // stays after the barrier so that pass 0 starts on the first chunk while
+  // later chunks are still arriving
+  clear_words<BLOCK>(&lds.hist[0][0], 3 * kBins + 3 * kSmallBins, t);
   lds_barrier();
   __builtin_amdgcn_sched_barrier(0);
+  uint32_t key[N];
 #pragma unroll
-  for (int i = 0; i < N; ++i) key[i] = score_key(key[i]);
+  for (int i = 0; i < N; ++i) key[i] = score_key(bits[i]);
 
-  // 2. radix select on the score keys
-  Radix sk{0u, 0u, static_cast<uint32_t>(k), 0u};
-  int pass = radix_select(lds, 0, key, valid, sk, t, lane, w);
-
-  // 3. id tie-break, only when the threshold key ties beyond what is needed
-  const bool tie = sk.count > sk.need;  // implies all three score passes ran
-  Radix ik{0u, 0u, sk.need, 0u};
-  uint32_t tied = 0;
-  uint32_t u[N];
+  // 2. pass 0: histogram of the top 11 bits; each item keeps its rank in its bin
+  uint32_t rank_in_bin[N];
+  if constexpr (FULL) {
 #pragma unroll
-  for (int i = 0; i < N; ++i) u[i] = ~idv[i];
-  bool dup = false;
-  uint32_t duprank[N];
-  if (tie) {
+    for (int i = 0; i < N; ++i) rank_in_bin[i] = lds_add(lds.hist[0] + (key[i] >> 21));
+  } else {
+    uint32_t* sink = lds.sink + lane;
 #pragma unroll
-    for (int i = 0; i < N; ++i) tied |= (((valid >> i) & 1u) && key[i] == sk.prefix) ? (1u << i) : 0u;
-    pass += radix_select(lds, pass, u, tied, ik, t, lane, w);
-    dup = ik.count > ik.need;  // identical (key, id) pairs straddle the boundary
-    if (dup) {
-      uint32_t same = 0;
-#pragma unroll
-      for (int i = 0; i < N; ++i) same |= (((tied >> i) & 1u) && u[i] == ik.prefix) ? (1u << i) : 0u;
-      position_scan<VEC, NV>(same, lds.segment[0], duprank, lane, w);
-    }
+    for (int i = 0; i < N; ++i) rank_in_bin[i] = lds_add((valid >> i) & 1u ? lds.hist[0] + (key[i] >> 21) : sink);
   }
+  lds_barrier();
+  Radix sk{0u, 0u, static_cast<uint32_t>(k), 0u};
+  advance(sk, find_digit<kBins>(lds.hist[0], sk.need, lane), 21, 0x7FFu);
 
-  // 4. stable compaction
-  uint32_t sel = 0;
+  const uint32_t m = sk.count;  // items in the threshold bin
+  bool tie = false, dup = false;
+  Radix ik{0u, 0u, 0u, 0u};
+  if (m != sk.need && m <= kListCap) {
+    // 3. the threshold bin as a list: each of its items writes itself at its
+    // rank and, in the same step, counts its next 8 key bits (list pass 0)
+    const uint32_t d0 = sk.prefix >> 21;
 #pragma unroll
-  for (int i = 0; i < N; ++i) {
-    const uint32_t kp = key[i] & sk.mask;
-    bool s = kp > sk.prefix;
-    if (kp == sk.prefix) {
-      if (!tie) {
-        s = true;
-      } else {
-        const uint32_t up = u[i] & ik.mask;
-        s = up > ik.prefix || (up == ik.prefix && (!dup || duprank[i] < ik.need));
+    for (int i = 0; i < N; ++i) {
+      if (((valid >> i) & 1u) && (key[i] >> 21) == d0) {
+        lds.list[rank_in_bin[i]] = make_uint2(key[i], idv[i]);
+        lds_add(lds.small[0] + ((key[i] >> 13) & 0xFFu));
       }
     }
-    sel |= (s && ((valid >> i) & 1u)) ? (1u << i) : 0u;
+    lds_barrier();
+    advance(sk, find_digit_small<kSmallBins>(lds.small[0], sk.need, lane), 13, 0xFFu);
+    int q = 1;
+    bool same_ids_known = false;
+    uint32_t uor = 0u, uand = 0u;
+    if (sk.count == m && m > sk.need) {
+      // everything fell into one bin again: look for bits shared by the whole
+      // list (identical scores, as on tie-heavy rows) and skip their passes
+      uint32_t kor, kand;
+      list_common_bits(lds, m, t, lane, w, kor, kand, uor, uand);
+      same_ids_known = true;
+      if (kor == kand) {  // every list item has the same key
+        sk.prefix = kor;
+        sk.mask = ~0u;
+      }
+    }
+    do {
+      if (sk.count == sk.need || sk.mask == ~0u) break;
+      list_pass<BLOCK, 5, 8, false>(lds, q++, m, 0u, sk, t, lane);
+      if (sk.count == sk.need) break;
+      list_pass<BLOCK, 0, 5, false>(lds, q++, m, 0u, sk, t, lane);
+    } while (false);
+    // 4. id tie-break over the list items with the threshold key (then all
+    // score bits are fixed and sk.prefix is the full threshold key)
+    tie = sk.count > sk.need;
+    if (tie) {
+      ik.need = sk.need;
+      ik.count = sk.count;
+      // id digits shared by every list item (so by every tied item) are fixed
+      // without a pass
+      const uint32_t differ = same_ids_known ? (uor ^ uand) : ~0u;
+      if ((differ >> 24) == 0u) { ik.prefix |= uand & 0xFF000000u; ik.mask |= 0xFF000000u; }
+      if ((differ >> 24) == 0u && ((differ >> 16) & 0xFFu) == 0u) { ik.prefix |= uand & 0x00FF0000u; ik.mask |= 0x00FF0000u; }
+      do {
+        if (!(ik.mask & 0xFF000000u)) list_pass<BLOCK, 24, 8, true>(lds, q++, m, sk.prefix, ik, t, lane);
+        if (ik.count == ik.need) break;
+        if (!(ik.mask & 0x00FF0000u)) list_pass<BLOCK, 16, 8, true>(lds, q++, m, sk.prefix, ik, t, lane);
+        if (ik.count == ik.need) break;
+        list_pass<BLOCK, 8, 8, true>(lds, q++, m, sk.prefix, ik, t, lane);
+        if (ik.count == ik.need) break;
+        list_pass<BLOCK, 0, 8, true>(lds, q++, m, sk.prefix, ik, t, lane);
+      } while (false);
+      dup = ik.count > ik.need;  // identical (key, id) pairs straddle the boundary
+    }
+  } else if (m != sk.need) {
+    // 3'. a bin too large for the list: the remaining passes over the registers
+    do {
+      radix_pass<BLOCK, 10, 11>(lds, 1, key, valid, sk, t, lane);
+      if (sk.count == sk.need) break;
+      radix_pass<BLOCK, 0, 10>(lds, 2, key, valid, sk, t, lane);
+    } while (false);
+    tie = sk.count > sk.need;
+    if (tie) {
+      uint32_t u[N], tied = 0;
+#pragma unroll
+      for (int i = 0; i < N; ++i) {
+        u[i] = ~idv[i];
+        tied |= (((valid >> i) & 1u) && key[i] == sk.prefix) ? (1u << i) : 0u;
+      }
+      ik.need = sk.need;
+      do {
+        radix_pass<BLOCK, 21, 11>(lds, 3, u, tied, ik, t, lane);
+        if (ik.count == ik.need) break;
+        radix_pass<BLOCK, 10, 11>(lds, 4, u, tied, ik, t, lane);
+        if (ik.count == ik.need) break;
+        radix_pass<BLOCK, 0, 10>(lds, 5, u, tied, ik, t, lane);
+      } while (false);
+      dup = ik.count > ik.need;
+    }
   }
+
+  uint32_t duprank[N];
+  if (dup) {
+    uint32_t same[N];
+#pragma unroll
+    for (int i = 0; i < N; ++i) same[i] = ((valid >> i) & 1u) & (key[i] == sk.prefix) & (~idv[i] == ik.prefix);
+    position_rank<BLOCK, VEC, N>(same, lds.segment[0], duprank, lane, w);
+  }
+  uint32_t sel[N];
+  if (!tie) {
+    // common case: sk.mask covers the top bits and sk.prefix is zero below
+    // them, so (key & mask) >= prefix is simply key >= prefix
+#pragma unroll
+    for (int i = 0; i < N; ++i) sel[i] = (key[i] >= sk.prefix) & ((valid >> i) & 1u);
+  } else {
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const uint32_t u = ~idv[i];
+      const bool wins = u >= ik.prefix && (u != ik.prefix || !dup || duprank[i] < ik.need);
+      sel[i] = (key[i] > sk.prefix || (key[i] == sk.prefix && wins)) & ((valid >> i) & 1u);
+    }
+  }
+
+  // 5. stable compaction and store
   uint32_t rank[N];
-  position_scan<VEC, NV>(sel, lds.segment[1], rank, lane, w);
+  position_rank<BLOCK, VEC, N>(sel, lds.segment[1], rank, lane, w);
+  const __amdgpu_buffer_rsrc_t dst = __builtin_amdgcn_make_buffer_rsrc(o, 0, k * static_cast<int>(sizeof(uint2)),
+                                                                        static_cast<int>(kBufferWord3));
 #pragma unroll
   for (int i = 0; i < N; ++i) {
-    if (((sel >> i) & 1u) && rank[i] < static_cast<uint32_t>(k)) o[rank[i]] = make_uint2(key_to_bits(key[i]), idv[i]);
+    const uint32_t off = sel[i] ? rank[i] * 8u : kDropOffset;
+    const int2v data = {static_cast<int>(bits[i]), static_cast<int>(idv[i])};
+    __builtin_amdgcn_raw_buffer_store_b64(data, dst, static_cast<int>(off), 0, 0);
   }
 }
 
-template <int VEC, int NV>
+template <int BLOCK, int VEC, int N>
 hipError_t launch(const dcp_topk_cand* cand, int32_t rows, int32_t num_cand, int32_t k, dcp_topk_cand* out,
                   hipStream_t stream) {
   void* args[] = {const_cast<dcp_topk_cand**>(&cand), &num_cand, &k, &out};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&stable_topk_select_kernel<VEC, NV>), dim3(rows),
-                         dim3(kBlock), args, 0, stream);
+  const void* fn = num_cand == BLOCK * N
+                       ? reinterpret_cast<const void*>(&stable_topk_select_kernel<BLOCK, VEC, N, true>)
+                       : reinterpret_cast<const void*>(&stable_topk_select_kernel<BLOCK, VEC, N, false>);
+  return hipLaunchKernel(fn, dim3(rows), dim3(BLOCK), args, 0, stream);
 }
 
 }  // namespace
 
 hipError_t launch_select(const dcp_topk_cand* cand, int32_t rows, int32_t num_cand, int32_t k, dcp_topk_cand* out,
                          hipStream_t stream) {
+  // 256 threads up to 2048 candidates, 512 above; the smallest item count per
+  // thread that covers the row.
   const bool vec2 = (num_cand % 2 == 0) && (reinterpret_cast<uintptr_t>(cand) % 16 == 0);
   if (vec2) {
-    if (num_cand <= 2 * kBlock) return launch<2, 1>(cand, rows, num_cand, k, out, stream);
-    if (num_cand <= 4 * kBlock) return launch<2, 2>(cand, rows, num_cand, k, out, stream);
-    if (num_cand <= 8 * kBlock) return launch<2, 4>(cand, rows, num_cand, k, out, stream);
-    return launch<2, 8>(cand, rows, num_cand, k, out, stream);
+    if (num_cand <= 512) return launch<256, 2, 2>(cand, rows, num_cand, k, out, stream);
+    if (num_cand <= 1024) return launch<256, 2, 4>(cand, rows, num_cand, k, out, stream);
+    if (num_cand <= 2048) return launch<256, 2, 8>(cand, rows, num_cand, k, out, stream);
+    if (num_cand <= 4096) return launch<512, 2, 8>(cand, rows, num_cand, k, out, stream);
+    if (num_cand <= 8192) return launch<512, 2, 16>(cand, rows, num_cand, k, out, stream);
+    return launch<512, 2, 32>(cand, rows, num_cand, k, out, stream);
   }
-  if (num_cand <= 2 * kBlock) return launch<1, 2>(cand, rows, num_cand, k, out, stream);
-  if (num_cand <= 4 * kBlock) return launch<1, 4>(cand, rows, num_cand, k, out, stream);
-  if (num_cand <= 8 * kBlock) return launch<1, 8>(cand, rows, num_cand, k, out, stream);
-  return launch<1, 16>(cand, rows, num_cand, k, out, stream);
+  if (num_cand <= 256) return launch<256, 1, 1>(cand, rows, num_cand, k, out, stream);
+  if (num_cand <= 512) return launch<256, 1, 2>(cand, rows, num_cand, k, out, stream);
+  if (num_cand <= 1024) return launch<256, 1, 4>(cand, rows, num_cand, k, out, stream);
+  if (num_cand <= 2048) return launch<256, 1, 8>(cand, rows, num_cand, k, out, stream);
+  if (num_cand <= 4096) return launch<512, 1, 8>(cand, rows, num_cand, k, out, stream);
+  if (num_cand <= 8192) return launch<512, 1, 16>(cand, rows, num_cand, k, out, stream);
+  return launch<512, 1, 32>(cand, rows, num_cand, k, out, stream);
 }
 
 }  // namespace dcptopk
