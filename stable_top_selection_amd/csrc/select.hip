@@ -129,12 +129,14 @@ __device__ __forceinline__ Digit find_digit(const uint32_t* hist, uint32_t need,
     sum += x.x + x.y + x.z + x.w;
   }
   const uint32_t incl = wave_inclusive_scan(sum, lane);
-  const int L = first_lane(__ballot(incl >= need));
+  // the forced top bits keep L and i inside the histogram even if `need`
+  // exceeded the total (the callers never let it)
+  const int L = first_lane(__ballot(incl >= need) | (1ull << 63));
   const uint32_t above_l = lane_of(incl, L) - lane_of(sum, L);
   const int top = NB - PER * L - 1;  // highest bin of lane L
   const uint32_t h = lane < PER ? hist[top - lane] : 0u;
   const uint32_t incl2 = wave_inclusive_scan(h, lane);
-  const int i = first_lane(__ballot(lane < PER && above_l + incl2 >= need));
+  const int i = first_lane(__ballot(lane < PER && above_l + incl2 >= need) | (1ull << (PER - 1)));
   Digit d;
   d.digit = static_cast<uint32_t>(top - i);
   d.count = lane_of(h, i);
@@ -166,7 +168,7 @@ __device__ __forceinline__ Digit find_digit_small(const uint32_t* hist, uint32_t
 #pragma unroll
   for (int j = 0; j < PER; ++j) sum += h[j];
   const uint32_t incl = wave_inclusive_scan(sum, lane);
-  const int L = first_lane(__ballot(lane < LANES && incl >= need));
+  const int L = first_lane(__ballot(lane < LANES && incl >= need) | (1ull << (LANES - 1)));
   uint32_t above = lane_of(incl, L) - lane_of(sum, L);
   Digit d{0u, 0u, 0u};
   bool found = false;
@@ -304,7 +306,8 @@ __device__ __forceinline__ void list_common_bits(SelectLds<BLOCK>& lds, int m, i
 // earlier slots of this thread.  `segment` must belong to this call alone.
 template <int BLOCK, int VEC, int N>
 __device__ __forceinline__ void position_rank(const uint32_t (&flag)[N], uint32_t* segment, uint32_t (&rank)[N],
-                                              int lane, int w) {
+                                              int lane, int w, uint32_t* wave_first = nullptr,
+                                              uint32_t* wave_count = nullptr) {
   constexpr int NV = N / VEC;       // chunks per thread
   constexpr int NW = (NV + 3) / 4;  // packed words: 4 chunk counts of 8 bits each
   constexpr int kWaves = BLOCK / kWave;
@@ -340,6 +343,8 @@ __device__ __forceinline__ void position_rank(const uint32_t (&flag)[N], uint32_
 #pragma unroll
   for (int i = 0; i < kWaves; ++i) before += i < w ? segment[i] : 0u;
   before = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(before)));
+  if (wave_first != nullptr) *wave_first = before;
+  if (wave_count != nullptr) *wave_count = wave_total;
 #pragma unroll
   for (int v = 0; v < NV; ++v) {
     uint32_t own = before + chunk_base[v] + ((excl[v / 4] >> (8 * (v % 4))) & 0xFFu);
@@ -542,16 +547,42 @@ __global__ __launch_bounds__(BLOCK) void stable_topk_select_kernel(const dcp_top
     }
   }
 
-  // 5. stable compaction and store
-  uint32_t rank[N];
-  position_rank<BLOCK, VEC, N>(sel, lds.segment[1], rank, lane, w);
+  // 5. stable compaction and store.  Wave w's selected items fill the output
+  // slots [out_first, out_first + out_count) (its positions precede all later waves'), so
+  // each wave stages its own items in LDS (the histograms and the list are
+  // dead by now: every wave is past position_rank's barrier) and writes its
+  // range with consecutive stores.  Unselected items write to this lane's own
+  // spare slot, so the staging loop has no per-item branch.
+  uint32_t rank[N], out_first, out_count;
+  position_rank<BLOCK, VEC, N>(sel, lds.segment[1], rank, lane, w, &out_first, &out_count);
   const __amdgpu_buffer_rsrc_t dst = __builtin_amdgcn_make_buffer_rsrc(o, 0, k * static_cast<int>(sizeof(uint2)),
                                                                         static_cast<int>(kBufferWord3));
+  // items a wave can stage: half of its slots, at most 512 (a wave past that
+  // stores straight from registers)
+  constexpr int kStageCap = kWave * N / 2 < 512 ? kWave * N / 2 : 512;
+  static_assert(sizeof(SelectLds<BLOCK>) >= (BLOCK / kWave) * (kStageCap + kWave) * sizeof(uint2), "staging fits");
+  if (out_count <= static_cast<uint32_t>(kStageCap)) {
+    uint2* stage = reinterpret_cast<uint2*>(&lds) + w * (kStageCap + kWave);
 #pragma unroll
-  for (int i = 0; i < N; ++i) {
-    const uint32_t off = sel[i] ? rank[i] * 8u : kDropOffset;
-    const int2v data = {static_cast<int>(bits[i]), static_cast<int>(idv[i])};
-    __builtin_amdgcn_raw_buffer_store_b64(data, dst, static_cast<int>(off), 0, 0);
+    for (int i = 0; i < N; ++i) {
+      const uint32_t slot = sel[i] ? rank[i] - out_first : static_cast<uint32_t>(kStageCap + lane);
+      stage[slot] = make_uint2(bits[i], idv[i]);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+    for (uint32_t e = lane; e < out_count; e += kWave) {
+      const uint2 x = stage[e];
+      const int2v data = {static_cast<int>(x.x), static_cast<int>(x.y)};
+      __builtin_amdgcn_raw_buffer_store_b64(data, dst, static_cast<int>((out_first + e) * 8u), 0, 0);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const uint32_t off = sel[i] ? rank[i] * 8u : kDropOffset;
+      const int2v data = {static_cast<int>(bits[i]), static_cast<int>(idv[i])};
+      __builtin_amdgcn_raw_buffer_store_b64(data, dst, static_cast<int>(off), 0, 0);
+    }
   }
 }
 

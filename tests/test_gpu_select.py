@@ -173,3 +173,52 @@ def test_graph_capture_replay_with_changing_inputs():
         from oracle import stable_topk as O
         ob, oi = O.select(g.scores, g.ids, k)
         assert np.array_equal(want_b, ob.view(np.uint32)) and np.array_equal(want_i, oi)
+
+
+def _sorted_within_ranks(g, descending=True):
+    """Each rank slice of every row sorted by score: the first chunk the kernel
+    sees is then far from a random sample of the row."""
+    scores, ids = g.scores.copy(), g.ids.copy()
+    lk = g.local_k
+    for r in range(g.dcp):
+        sl = slice(r * lk, (r + 1) * lk)
+        order = np.argsort(scores[:, sl], axis=1, kind="stable")
+        if descending:
+            order = order[:, ::-1]
+        scores[:, sl] = np.take_along_axis(scores[:, sl], order, axis=1)
+        ids[:, sl] = np.take_along_axis(ids[:, sl], order, axis=1)
+    return scores, ids
+
+
+@pytest.mark.parametrize("descending", [True, False])
+def test_rank_slices_sorted_by_score(descending):
+    """Local top-K outputs are often sorted; the selection must not depend on
+    the order of the candidates within a row."""
+    for g in (W.decode(16), W.large(rows=32), W.tie_heavy(16)):
+        s, i = _sorted_within_ranks(g, descending)
+        assert_select_parity(s, i, g.k, f"{g.name} sorted desc={descending}")
+
+
+def test_threshold_bin_sizes():
+    """Threshold bins of about 1.5k items (more than one window segment holds)
+    and of the whole row with distinct low bits (more than a list holds)."""
+    rng = np.random.default_rng(71)
+    rows, c, k = 6, 8192, 2048
+    # ~1500 items share the threshold's top 11 bits: 1.5k values in [1, 1.0625)
+    base = rng.standard_normal((rows, c)).astype(np.float32) * np.float32(0.01)
+    near = (np.float32(1.0) + rng.random((rows, 1500), dtype=np.float32) * np.float32(0.0624)).astype(np.float32)
+    s = np.concatenate([np.full((rows, 1000), 50.0, np.float32), near, base[:, : c - 2500]], axis=1)
+    s = np.ascontiguousarray(np.take_along_axis(s, rng.permuted(np.tile(np.arange(c), (rows, 1)), axis=1), axis=1))
+    ids = W.distinct_per_row(rng, rows, c, 4 * c)
+    assert_select_parity(s, ids, k, "threshold bin ~1500")
+    # every key shares its top 11 bits, the low bits differ
+    s = (np.float32(1.0) + rng.random((rows, c), dtype=np.float32) * np.float32(0.0009)).astype(np.float32)
+    assert_select_parity(s, ids, k, "one bin, distinct low bits")
+    assert_select_parity(s, ids, 1, "one bin, k=1")
+
+
+@pytest.mark.parametrize("rows,c,k", [(3, 2600, 1000), (3, 2560, 7), (2, 5000, 4999), (2, 9000, 3000)])
+def test_rows_shorter_than_the_thread_slots(rows, c, k):
+    """Rows whose last waves hold no candidate at all."""
+    g = W.random_gathered(rows, c, k, seed=c, dist="uniform")
+    assert_select_parity(g.scores, g.ids, k, g.name, guard=1)
