@@ -14,6 +14,11 @@ Sources (vLLM pull-request pages):
   selection is deterministic.  The selector it replaced always sorted a 64-bit
   key whose high word is the 32-bit score key and whose low word is the bitwise
   complement of the token id; the new selector works on 32-bit score keys first.
+* PR #50009, "[DCP][Performance] Add Shared-DCP peer-addressable decode data
+  paths", Top-K performance: the stable top-K consumer can load every owner's
+  candidate shard in place rather than from a gathered copy (the fused merge
+  computes the same result as ``merge``); each rank keeps 2048 candidates out
+  of 4096 local score columns (the local top-K step, ``local_topk``).
 * PR #59367, "[Bugfix][Attention] Reserve the sparse indexer's DCP top-k merge
   scratch through the workspace manager", Purpose: the pack step turns each
   rank's local top-K into packed (score, global id) candidates using a per-row
@@ -38,6 +43,11 @@ Readings where the pages leave a step open (each is pinned by a test, see
    padding candidate (-inf, INT32_MAX).
 6. Pack: global id = local index + row start + rank offset, wrapped to int32;
    a negative local index marks an invalid slot and packs to (-inf, INT32_MAX).
+7. Local top-K (its tie rule is not on the pages): the merge's order with the
+   column as the id, so equal scores go to the lowest column; the selected
+   columns are written in column order; a row with fewer valid columns than k
+   (per-row lengths) is followed by (-inf, -1) slots, the invalid local slot
+   that the pack step recognises.
 """
 from __future__ import annotations
 
@@ -102,6 +112,43 @@ def select(scores: np.ndarray, ids: np.ndarray, k: int, row_block: int = 256):
         out_bits[r0:r1, :n_sel] = np.take_along_axis(score_bits[r0:r1], chosen, axis=1)
         out_ids[r0:r1, :n_sel] = np.take_along_axis(ids[r0:r1], chosen, axis=1)
     return out_bits.view(np.float32), out_ids
+
+
+LOCAL_PAD_INDEX = np.int32(-1)
+
+
+def local_topk(scores: np.ndarray, k: int, lengths: np.ndarray | None = None):
+    """One rank's local top-K of its indexer scores (reading 7).
+
+    PR #47348, Summary: every DCP rank holds the local top-K of its shard;
+    PR #50009, Top-K performance: 2048 of 4096 local score columns.
+    ``scores`` float32 (rows, num_cols); ``lengths`` int32 (rows,) or None
+    (row t's candidates are its first clamp(lengths[t], 0, num_cols) columns).
+    Returns (out_scores float32 (rows, k), out_idx int32 (rows, k)).
+
+    Per row: order the valid columns by score key, largest first, and among
+    equal keys by column, lowest first; keep the first min(k, len); write them
+    in column order; fill the remaining slots with (-inf, -1).
+    """
+    scores = np.ascontiguousarray(scores, dtype=np.float32)
+    if scores.ndim != 2:
+        raise ValueError("scores must be (rows, num_cols)")
+    if k < 1:
+        raise ValueError("k must be >= 1")
+    rows, num_cols = scores.shape
+    out_bits = np.full((rows, k), PAD_SCORE_BITS, dtype=np.uint32)
+    out_idx = np.full((rows, k), LOCAL_PAD_INDEX, dtype=np.int32)
+    bits = scores.view(np.uint32)
+    for t in range(rows):
+        n = num_cols if lengths is None else int(min(max(int(lengths[t]), 0), num_cols))
+        key = score_key(scores[t, :n])
+        # ascending stable sort of the complemented key: largest key first,
+        # equal keys in column order
+        order = np.argsort(~key, kind="stable")
+        chosen = np.sort(order[:min(k, n)])
+        out_bits[t, :chosen.size] = bits[t, chosen]
+        out_idx[t, :chosen.size] = chosen.astype(np.int32)
+    return out_bits.view(np.float32), out_idx
 
 
 def pack(local_scores: np.ndarray, local_idx: np.ndarray, row_starts: np.ndarray, rank_offset: int):

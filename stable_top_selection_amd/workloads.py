@@ -30,6 +30,15 @@ Recipes (numpy PCG64, ``np.random.default_rng(seed)``):
                  offsets r * 135168 (131072 + 4096, the smallest stride that keeps
                  the ranks' id ranges disjoint).
 
+* ``fused``      the prefill recipe at 256 rows (seed 7): the per-rank arrays
+                 that the fused merge reads in place, the same shape as
+                 ``large`` (8192 candidates per row, K 2048).
+* ``local``      one rank's indexer scores before its local top-K: rows 64 (also
+                 1/8/32 and 256), 4096 columns, k 2048 (vLLM PR #50009, "Add
+                 Shared-DCP peer-addressable decode data paths", Top-K
+                 performance: 2048 candidates per rank out of 4096 local score
+                 columns), scores N(0,1); optional per-row lengths U[0, 4096].
+
 Within a rank's slice, candidates appear in generation order (neither scores nor
 ids are sorted).
 """
@@ -115,6 +124,25 @@ class LocalShards:
         return h.hexdigest()[:16]
 
 
+@dataclass
+class DenseScores:
+    """One rank's indexer scores: ``scores`` (rows, num_cols) float32 and, if
+    not None, ``lengths`` (rows,) int32 valid columns per row."""
+
+    name: str
+    scores: np.ndarray
+    k: int
+    lengths: np.ndarray | None = None
+
+    @property
+    def rows(self) -> int:
+        return int(self.scores.shape[0])
+
+    @property
+    def num_cols(self) -> int:
+        return int(self.scores.shape[1])
+
+
 def distinct_per_row(rng: np.random.Generator, rows: int, count: int, span: int) -> np.ndarray:
     """(rows, count) int32: each row holds ``count`` distinct ints from [0, span)."""
     if count > span:
@@ -173,16 +201,46 @@ def tie_heavy(rows: int = 16, seed: int = 4) -> Gathered:
                     local_k=local_k, meta={"empty_shards": empty})
 
 
-def prefill(rows: int = 8192, seed: int = 5, dcp: int = 4, local_k: int = 2048) -> LocalShards:
+def prefill(rows: int = 8192, seed: int = 5, dcp: int = 4, local_k: int = 2048,
+            invalid_frac: float = 0.0) -> LocalShards:
+    """``invalid_frac`` of the local slots, chosen at random after the draws
+    above, get local index -1 (an invalid slot)."""
     rng = np.random.default_rng(seed)
     scores = rng.standard_normal((dcp, rows, local_k), dtype=np.float32)
     local_idx = np.empty((dcp, rows, local_k), dtype=np.int32)
     for r in range(dcp):
-        local_idx[r] = distinct_per_row(rng, rows, local_k, PREFILL_LOCAL_COLUMNS)
+        local_idx[r] = distinct_per_row(rng, rows, local_k, max(PREFILL_LOCAL_COLUMNS, local_k))
     starts = rng.integers(0, PREFILL_ROW_START_SPAN, size=rows, dtype=np.int32)
     row_starts = np.ascontiguousarray(np.broadcast_to(starts, (dcp, rows)))
     rank_offsets = (np.arange(dcp, dtype=np.int32) * np.int32(PREFILL_RANK_STRIDE)).astype(np.int32)
+    if invalid_frac > 0.0:
+        local_idx = np.where(rng.random(local_idx.shape) < invalid_frac, np.int32(-1), local_idx).astype(np.int32)
     return LocalShards(f"prefill_T{rows}", scores, local_idx, row_starts, rank_offsets, k=2048)
+
+
+def fused(rows: int = 256, seed: int = 7) -> LocalShards:
+    sh = prefill(rows=rows, seed=seed)
+    sh.name = f"fused_rows{rows}"
+    return sh
+
+
+def local(rows: int = 64, num_cols: int = 4096, k: int = 2048, seed: int | None = None,
+          dist: str = "normal", with_lengths: bool = False) -> DenseScores:
+    """``dist``: ``normal`` (N(0,1)), ``levels`` (the 16 tie levels) or
+    ``special`` (the +-0 / +-inf / finite mix of ``random_gathered``)."""
+    rng = np.random.default_rng([6, rows, num_cols, k] if seed is None else seed)
+    shape = (rows, num_cols)
+    if dist == "normal":
+        scores = rng.standard_normal(shape, dtype=np.float32)
+    elif dist == "levels":
+        scores = TIE_LEVELS[rng.integers(0, 16, size=shape)]
+    elif dist == "special":
+        alphabet = np.array([-np.inf, -2.0, -1.0, -0.0, 0.0, 1.0, 2.0, np.inf], dtype=np.float32)
+        scores = alphabet[rng.integers(0, alphabet.size, size=shape)]
+    else:
+        raise ValueError(dist)
+    lengths = rng.integers(0, num_cols + 1, size=rows, dtype=np.int32) if with_lengths else None
+    return DenseScores(f"local_{dist}_{rows}x{num_cols}_k{k}", np.ascontiguousarray(scores), k=k, lengths=lengths)
 
 
 def random_gathered(rows: int, num_cand: int, k: int, seed: int, dist: str = "normal",

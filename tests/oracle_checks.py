@@ -385,6 +385,85 @@ def check_pages_memory_figures():
         assert ws == O.gather_output_bytes(min(rows, 1024), 4, 2048)
 
 
+# ----------------------------------------------------------------------------
+# local top-K (the step before the merge)
+# ----------------------------------------------------------------------------
+def _brute_local_row(bits, k, length):
+    """Brute-force local top-K of one row: the candidates are the first
+    ``length`` columns with id = column; then (-inf, -1) slots."""
+    n = len(bits) if length is None else min(max(int(length), 0), len(bits))
+    cols = list(range(n))
+    eb, ei = brute_select_row([int(b) for b in bits[:n]], cols, k) if n else ([], [])
+    m = min(k, n)
+    return eb[:m] + [PAD_BITS] * (k - m), ei[:m] + [-1] * (k - m)
+
+
+def check_local_topk_against_brute(seed=11):
+    """Small rows with heavy ties, +-0, +-inf and per-row lengths (including
+    0, negative and past the end) against the O(C^2) brute force."""
+    rng = np.random.default_rng(seed)
+    for dist in ("levels", "special", "normal"):
+        for num_cols, k in ((1, 1), (7, 3), (40, 40), (40, 64), (96, 17)):
+            d = W.local(rows=5, num_cols=num_cols, k=k, seed=int(rng.integers(1 << 30)), dist=dist)
+            lengths = np.array([num_cols, 0, -3, num_cols + 5, num_cols // 2], np.int32)
+            for lens in (None, lengths):
+                s, i = O.local_topk(d.scores, k, lens)
+                sb = np.asarray(s, np.float32).view(np.uint32)
+                for t in range(d.rows):
+                    eb, ei = _brute_local_row(d.scores[t].view(np.uint32), k, None if lens is None else lens[t])
+                    assert [int(x) for x in sb[t]] == eb, (dist, num_cols, k, t)
+                    assert [int(x) for x in i[t]] == ei, (dist, num_cols, k, t)
+
+
+def check_local_topk_distinct_matches_library_topk(seed=12):
+    """Distinct scores: the selected columns are torch.topk's, in column order,
+    with their scores copied."""
+    import torch
+
+    rng = np.random.default_rng(seed)
+    # distinct, exactly representable scores (-8 .. 8 in steps of 2^-8)
+    scores = np.stack([rng.permutation(4096) for _ in range(8)]).astype(np.float32) / np.float32(256) - np.float32(8)
+    s, i = O.local_topk(scores, 2048)
+    ref = torch.topk(torch.from_numpy(scores), 2048, dim=1).indices.sort(dim=1).values.numpy()
+    assert np.array_equal(i, ref.astype(np.int32))
+    assert np.array_equal(s.view(np.uint32), np.take_along_axis(scores, ref, 1).view(np.uint32))
+
+
+def check_local_topk_all_ties_take_first_columns():
+    """A constant row keeps columns 0..k-1; a row of -inf scores too."""
+    for value in (1.0, -np.inf):
+        scores = np.full((2, 300), value, np.float32)
+        s, i = O.local_topk(scores, 120)
+        assert np.array_equal(i, np.broadcast_to(np.arange(120, dtype=np.int32), (2, 120)))
+
+
+def check_local_then_merge_is_global_topk(seed=13):
+    """Two stages equal one (PR #47348, Summary: each rank keeps the top-K of
+    its shard, the merge takes the global top-K): local top-K per rank with ids
+    made global by the pack, then the merge, equals the top-K of the
+    concatenated score rows with global ids, written out here column by
+    column, in the same position order."""
+    rng = np.random.default_rng(seed)
+    dcp, rows, cols, k = 4, 6, 96, 40
+    for dist in ("levels", "normal"):
+        ranks = [W.local(rows=rows, num_cols=cols, k=k, seed=int(rng.integers(1 << 30)), dist=dist)
+                 for _ in range(dcp)]
+        starts = rng.integers(0, 1000, size=rows, dtype=np.int32)
+        offs = np.arange(dcp, dtype=np.int32) * np.int32(1000 + cols)
+        loc = [O.local_topk(d.scores, k) for d in ranks]
+        ms, mi = O.merge(np.stack([l[0] for l in loc]), np.stack([l[1] for l in loc]),
+                         np.stack([starts] * dcp), offs, k)
+        bits = np.concatenate([d.scores.view(np.uint32) for d in ranks], axis=1)
+        gid = np.empty((rows, dcp * cols), np.int32)
+        for r in range(dcp):
+            for c in range(cols):
+                gid[:, r * cols + c] = c + starts + offs[r]
+        for t in range(rows):
+            eb, ei = brute_select_row(bits[t], gid[t], k)
+            assert [int(x) for x in ms[t].view(np.uint32)] == eb, (dist, t)
+            assert [int(x) for x in mi[t]] == ei, (dist, t)
+
+
 ALL_CHECKS = [
     check_score_key_ladder,
     check_score_key_orders_like_floats,
@@ -401,4 +480,8 @@ ALL_CHECKS = [
     check_merge_hand_example,
     check_merge_equals_select_of_gathered,
     check_pages_memory_figures,
+    check_local_topk_against_brute,
+    check_local_topk_distinct_matches_library_topk,
+    check_local_topk_all_ties_take_first_columns,
+    check_local_then_merge_is_global_topk,
 ]

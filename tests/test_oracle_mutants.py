@@ -14,6 +14,7 @@ from oracle import stable_topk as O
 
 _ORIG_SCORE_KEY = O.score_key
 _ORIG_PACK = O.pack
+_ORIG_LOCAL = O.local_topk
 
 
 def _key_no_negative_flip(scores):
@@ -86,6 +87,31 @@ def _gather_reversed(local_scores, local_idx, row_starts, rank_offsets):
     return np.concatenate([p[0] for p in parts], axis=1), np.concatenate([p[1] for p in parts], axis=1)
 
 
+def _make_local(mistake):
+    def local_topk(scores, k, lengths=None):
+        scores = np.ascontiguousarray(scores, dtype=np.float32)
+        rows, num_cols = scores.shape
+        if mistake == "ignores_lengths":
+            return _ORIG_LOCAL(scores, k, None)
+        out_bits = np.full((rows, k), np.uint32(0xFF800000), dtype=np.uint32)
+        out_idx = np.full((rows, k), np.int32(2**31 - 1) if mistake == "pad_intmax" else np.int32(-1), np.int32)
+        for t in range(rows):
+            n = num_cols if lengths is None else int(min(max(int(lengths[t]), 0), num_cols))
+            key = O.score_key(scores[t, :n])
+            if mistake == "ties_highest_column":
+                order = np.argsort(key, kind="stable")[::-1]
+            else:
+                order = np.argsort(~key, kind="stable")
+            chosen = order[:min(k, n)]
+            if mistake != "score_order_output":
+                chosen = np.sort(chosen)
+            out_bits[t, :chosen.size] = scores[t].view(np.uint32)[chosen]
+            out_idx[t, :chosen.size] = chosen
+        return out_bits.view(np.float32), out_idx
+
+    return local_topk
+
+
 MUTANTS = {
     "key_no_negative_flip": ("score_key", _key_no_negative_flip),
     "key_sign_xor_only": ("score_key", _key_sign_xor_only),
@@ -101,6 +127,10 @@ MUTANTS = {
     "gather_ranks_reversed": ("gather_rows", _gather_reversed),
     "scratch_one_dcp_term": ("pages_scratch_bytes", lambda rows, dcp, k: (1 + dcp) * 8 * rows * k),
     "workspace_not_chunked": ("merge_workspace_bytes", lambda rows, dcp, k: rows * dcp * k * 8),
+    "local_ties_highest_column": ("local_topk", _make_local("ties_highest_column")),
+    "local_score_order_output": ("local_topk", _make_local("score_order_output")),
+    "local_pad_intmax": ("local_topk", _make_local("pad_intmax")),
+    "local_ignores_lengths": ("local_topk", _make_local("ignores_lengths")),
 }
 
 
