@@ -17,8 +17,9 @@ reported separately and labelled.
 
 Other lines of the same JSON object: the decode rows sweep and the tie-heavy
 workload as latencies, the chunked prefill merge (T = 8192) as a whole-driver
-time, the CPU oracle timed on the host (``cpu_baseline``), and the roofline of
-the select kernel.
+time, the fused merge (no gathered buffer) on the large shape and on the
+prefill workload, the local top-K (2048 of 4096 columns), the CPU oracle timed
+on the host (``cpu_baseline``), and the roofline of the select kernel.
 """
 from __future__ import annotations
 
@@ -53,9 +54,9 @@ def parse_args():
     p.add_argument("--steps", type=int, default=200, help="select launches per timed trial")
     p.add_argument("--warmup", type=int, default=20, help="untimed launches before timing")
     p.add_argument("--trials", type=int, default=7)
-    p.add_argument("--configs", default="large,large_warm,large_eager,decode,tie_heavy,prefill",
-                   help="comma list of large_warm, large_eager, decode, tie_heavy, prefill; the cold large "
-                        "headline always runs (--configs large runs it alone, as profiled)")
+    p.add_argument("--configs", default="large,large_warm,large_eager,decode,tie_heavy,prefill,fused,local",
+                   help="comma list of large_warm, large_eager, decode, tie_heavy, prefill, fused, local; the "
+                        "cold large headline always runs (--configs large runs it alone, as profiled)")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU oracle work to time")
     p.add_argument("--pmc", action="store_true",
@@ -261,6 +262,146 @@ def bench_prefill(run, trials):
             "rows_checked": int(len(rows))}
 
 
+class RankPtrs:
+    """Host arrays of one launch's per-rank device pointers (kept alive)."""
+
+    def __init__(self, scores, idx, starts, offsets):
+        import ctypes
+
+        n = len(scores)
+        arr = ctypes.c_void_p * n
+        self.s = arr(*[t.data_ptr() for t in scores])
+        self.i = arr(*[t.data_ptr() for t in idx])
+        self.r = arr(*[t.data_ptr() for t in starts])
+        self.o = (ctypes.c_int32 * n)(*[int(x) for x in offsets])
+        self.args = [ctypes.cast(x, ctypes.c_void_p) for x in (self.s, self.i, self.r, self.o)]
+
+
+def bench_fused(run, steps, warmup, trials):
+    """The fused merge (select straight from the ranks' local arrays):
+    (1) on the large shape (256 rows, DCP 4 x local K 2048, K 2048), HBM-cold
+    pool, per launch; (2) on the prefill workload, all T = 8192 rows in one
+    launch, against the chunked merge of the same inputs."""
+    import numpy as np
+
+    from oracle import stable_topk as oracle
+    from stable_top_selection_amd import workloads as W
+
+    torch = run.torch
+    to = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(run.dev)  # noqa: E731
+    res = {}
+
+    sh = W.fused()
+    dcp, rows, lk, k = sh.dcp, sh.rows, sh.local_k, sh.k
+    per = select_bytes(rows, dcp * lk, k)
+    n = max(1, -(-COLD_POOL_BYTES // per))
+    sc = to(sh.scores).unsqueeze(0).repeat(n, 1, 1, 1)
+    ix = to(sh.local_idx).unsqueeze(0).repeat(n, 1, 1, 1)
+    rs = [to(sh.row_starts[r]) for r in range(dcp)]
+    outs = torch.empty((n, rows, k, 2), dtype=torch.int32, device=run.dev)
+    ptrs = [RankPtrs([sc[i, r] for r in range(dcp)], [ix[i, r] for r in range(dcp)], rs, sh.rank_offsets)
+            for i in range(n)]
+
+    def launch(i):
+        def f(sp):
+            st = run.lib.dcp_topk_merge_fused(*ptrs[i % n].args, dcp, rows, lk, k, outs[i % n].data_ptr(), sp)
+            if st != 0:
+                raise RuntimeError(run.B.status_string(st))
+        return f
+
+    for i in range(warmup):
+        launch(i)(run.stream_ptr())
+    launches = max(steps, n)
+    graph = run.graph_of([launch(i) for i in range(launches)])
+    ms = run.time_graph(graph, trials)
+    us = statistics.median([1e3 * m / launches for m in ms])
+    want_s, want_i = oracle.merge(sh.scores, sh.local_idx, sh.row_starts, sh.rank_offsets, k)
+    for i in (0, n - 1):
+        o = outs[i].cpu().numpy()
+        if not (np.array_equal(o[..., 0].view(np.uint32), want_s.view(np.uint32)) and np.array_equal(o[..., 1], want_i)):
+            raise AssertionError("fused merge output differs from the oracle")
+    fused_bytes = per + dcp * rows * 4
+    res["large_shape_cold"] = {"workload": f"{sh.name}: {rows} rows, DCP {dcp} x local K {lk}, K {k}",
+                               "us_per_launch": round(us, 3), "pool_buffers": n, "launches": launches,
+                               "GBps": round(fused_bytes / (us * 1e-6) / 1e9, 1),
+                               "algorithmic_bytes_per_launch": fused_bytes}
+    del graph, sc, ix, outs, ptrs
+    torch.cuda.empty_cache()
+
+    sh = W.prefill()
+    dcp, T, lk, k = sh.dcp, sh.rows, sh.local_k, sh.k
+    sc = [to(sh.scores[r]) for r in range(dcp)]
+    ix = [to(sh.local_idx[r]) for r in range(dcp)]
+    rs = [to(sh.row_starts[r]) for r in range(dcp)]
+    out = torch.empty((T, k, 2), dtype=torch.int32, device=run.dev)
+    rp = RankPtrs(sc, ix, rs, sh.rank_offsets)
+
+    def fused(sp):
+        st = run.lib.dcp_topk_merge_fused(*rp.args, dcp, T, lk, k, out.data_ptr(), sp)
+        if st != 0:
+            raise RuntimeError(run.B.status_string(st))
+
+    graph = run.graph_of([fused])
+    ms = statistics.median(run.time_graph(graph, trials))
+    rows = np.unique(np.concatenate([np.arange(0, T, 97), [1023, 1024, 4095, 4096, T - 1]]))
+    want_s, want_i = oracle.merge(sh.scores[:, rows], sh.local_idx[:, rows], sh.row_starts[:, rows],
+                                  sh.rank_offsets, k)
+    o = out.cpu().numpy()[rows]
+    if not (np.array_equal(o[..., 0].view(np.uint32), want_s.view(np.uint32)) and np.array_equal(o[..., 1], want_i)):
+        raise AssertionError("fused prefill merge differs from the oracle on sampled rows")
+    pre_bytes = T * dcp * lk * 8 + T * k * 8 + dcp * T * 4
+    res["prefill_one_launch"] = {"workload": f"prefill: T={T}, DCP {dcp} x local K {lk}, K {k}, one launch",
+                                 "ms": round(ms, 4), "GBps": round(pre_bytes / (ms * 1e-3) / 1e9, 1),
+                                 "rows_checked": int(len(rows))}
+    return res
+
+
+def bench_local(run, steps, warmup, trials):
+    """Local top-K, 2048 of 4096 columns per row: rows 64 (the largest decode
+    row count measured on PR #50009) and 256, HBM-cold pools, and rows 64 warm."""
+    import numpy as np
+
+    from oracle import stable_topk as oracle
+    from stable_top_selection_amd import workloads as W
+
+    torch = run.torch
+    res = {}
+    for rows, cold in ((64, True), (64, False), (256, True)):
+        d = W.local(rows=rows)
+        cols, k = d.num_cols, d.k
+        per = rows * cols * 4 + rows * k * 8
+        n = max(1, -(-COLD_POOL_BYTES // per)) if cold else 1
+        src = torch.from_numpy(d.scores).to(run.dev).unsqueeze(0).repeat(n, 1, 1)
+        os_ = torch.empty((n, rows, k), dtype=torch.float32, device=run.dev)
+        oi = torch.empty((n, rows, k), dtype=torch.int32, device=run.dev)
+
+        def launch(i):
+            def f(sp):
+                st = run.lib.dcp_topk_local(src[i % n].data_ptr(), cols, None, rows, cols, k, os_[i % n].data_ptr(),
+                                            oi[i % n].data_ptr(), k, sp)
+                if st != 0:
+                    raise RuntimeError(run.B.status_string(st))
+            return f
+
+        for i in range(warmup):
+            launch(i)(run.stream_ptr())
+        launches = max(steps, n)
+        graph = run.graph_of([launch(i) for i in range(launches)])
+        us = statistics.median([1e3 * m / launches for m in run.time_graph(graph, trials)])
+        ws, wi = oracle.local_topk(d.scores, k)
+        for i in (0, n - 1):
+            if not (np.array_equal(os_[i].cpu().numpy().view(np.uint32), ws.view(np.uint32))
+                    and np.array_equal(oi[i].cpu().numpy(), wi)):
+                raise AssertionError(f"local top-K output differs from the oracle ({d.name})")
+        res[f"rows{rows}_{'cold' if cold else 'warm'}"] = {
+            "us_per_launch": round(us, 3), "GBps": round(per / (us * 1e-6) / 1e9, 1), "pool_buffers": n,
+            "algorithmic_bytes_per_launch": per}
+        del graph, src, os_, oi
+        torch.cuda.empty_cache()
+    res["workload"] = "local top-K: 4096 fp32 columns per row, k 2048, scores N(0,1)"
+    return res
+
+
 def cpu_baseline(g, seconds):
     """The CPU oracle (numpy, single-threaded sort) on the same workload."""
     from oracle import stable_topk as oracle
@@ -366,6 +507,12 @@ def main():
     if "prefill" in configs:
         extra["prefill"] = bench_prefill(run, args.trials)
         log(f"[prefill] {extra['prefill']}")
+    if "fused" in configs:
+        extra["fused_merge"] = bench_fused(run, args.steps, args.warmup, args.trials)
+        log(f"[fused] {extra['fused_merge']}")
+    if "local" in configs:
+        extra["local_topk"] = bench_local(run, args.steps, args.warmup, args.trials)
+        log(f"[local] {extra['local_topk']}")
 
     cpu = None
     if not args.no_cpu:
@@ -392,7 +539,7 @@ def main():
         "us_per_launch": us,
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": traffic,
-                     "kernel": "stable_topk_select_kernel<2,4>", "algorithmic_bytes_per_launch": per_launch_bytes},
+                     "kernel": "stable_topk_kernel<512, 2, 16, full, GatheredSource, PairSink>", "algorithmic_bytes_per_launch": per_launch_bytes},
         "cpu_baseline": cpu,
         "context": {"pages_selector_us_rows256_c8192": 15.459,
                     "pages_note": "PR #47348 Benchmarks, median of 7x200 launches; hardware and K not stated"},

@@ -54,8 +54,9 @@ extern "C" {
  * the rows 1024 at a time so its scratch stays bounded). */
 #define DCP_TOPK_MERGE_ROWS 1024
 
-/* Largest candidate count per row that dcp_topk_select accepts.  The pages
- * benchmark rows of 4096, 8192 and 16384 candidates (PR #47348, Benchmarks). */
+/* Largest candidate count per row, and largest k, that the entry points
+ * accept.  The pages benchmark rows of 4096, 8192 and 16384 candidates
+ * (PR #47348, Benchmarks). */
 #define DCP_TOPK_MAX_CANDIDATES 16384
 
 /* Alignment the chunked merge requires of its workspace, in bytes. */
@@ -73,9 +74,10 @@ enum {
   DCP_TOPK_OK = 0,
   DCP_TOPK_EINVAL = -1,       /* bad argument: null pointer, negative size,
                                  k < 1, misaligned or overlapping buffers */
-  DCP_TOPK_EUNSUPPORTED = -2, /* valid but unsupported shape (num_cand above
-                                 DCP_TOPK_MAX_CANDIDATES); the caller can fall
-                                 back to another selector */
+  DCP_TOPK_EUNSUPPORTED = -2, /* valid but unsupported shape (num_cand or k
+                                 above DCP_TOPK_MAX_CANDIDATES, or a limit of
+                                 one entry point); the caller can fall back to
+                                 another selector */
   DCP_TOPK_EWORKSPACE = -3,   /* workspace too small or not 256-byte aligned */
   DCP_TOPK_EHIP = -4          /* the HIP runtime rejected a launch */
 };
@@ -171,6 +173,63 @@ DCP_TOPK_API int dcp_topk_merge_chunked(const float* const* local_scores, const 
                            const int32_t* const* row_starts, const int32_t* rank_offsets, int32_t dcp,
                            int32_t rows, int32_t local_k, int32_t k, void* workspace,
                            size_t workspace_bytes, dcp_topk_cand* out, hipStream_t stream);
+
+/* Most DCP ranks dcp_topk_merge_fused reads in one call. */
+#define DCP_TOPK_FUSED_MAX_RANKS 16
+
+/*
+ * dcp_topk_merge_fused — the merge without a gathered buffer: the selector
+ * reads every rank's local top-K arrays in place and packs each candidate as
+ * it loads it.  This is the one-GPU form of the consumer in vLLM PR #50009
+ * ("[DCP][Performance] Add Shared-DCP peer-addressable decode data paths",
+ * Top-K performance), where the stable top-K loads each owner's candidate
+ * shard through local and peer views instead of from an all-gathered copy; it
+ * removes the write and re-read of the packed buffer that
+ * dcp_topk_merge_chunked makes.
+ *
+ *   local_scores, local_idx, row_starts, rank_offsets, dcp, rows, k, out
+ *                 as in dcp_topk_merge_chunked
+ *   local_k       a multiple of 64 (so that no wave's load straddles two
+ *                 ranks); other values return DCP_TOPK_EUNSUPPORTED
+ *
+ * Limits (DCP_TOPK_EUNSUPPORTED): dcp <= DCP_TOPK_FUSED_MAX_RANKS, dcp *
+ * local_k <= DCP_TOPK_MAX_CANDIDATES.  No workspace and no chunking: all rows
+ * go in one launch.  The result is bit-identical to dcp_topk_merge_chunked
+ * with the same arguments (so to dcp_topk_pack of every rank followed by
+ * dcp_topk_select); out must not overlap any input (DCP_TOPK_EINVAL).
+ */
+DCP_TOPK_API int dcp_topk_merge_fused(const float* const* local_scores, const int32_t* const* local_idx,
+                         const int32_t* const* row_starts, const int32_t* rank_offsets, int32_t dcp,
+                         int32_t rows, int32_t local_k, int32_t k, dcp_topk_cand* out, hipStream_t stream);
+
+/*
+ * dcp_topk_local — the step before the merge: every rank's local top-K of
+ * its indexer scores.  PR #47348 (Summary) has each DCP rank hold the local
+ * top-K of its shard of the KV cache; PR #50009 (Top-K performance) measures
+ * 2048 candidates per rank taken from 4096 local score columns.  The pages do
+ * not state this step's tie rule; this library uses the merge's: for each row
+ * t the candidates are the columns c < len(t), with score scores[t, c] and id
+ * c, ordered by score key descending then by lowest column, and the min(k,
+ * len(t)) best are written in column order, followed by (-inf, -1) slots,
+ * which dcp_topk_pack turns into its padding candidate.  The output is
+ * exactly the (local_scores, local_idx) pair that dcp_topk_pack,
+ * dcp_topk_merge_chunked and dcp_topk_merge_fused take.
+ *
+ *   scores            device, fp32, rows x num_cols, row stride
+ *                     score_row_stride (>= num_cols) elements
+ *   lengths           device int32[rows], or NULL; len(t) = lengths[t]
+ *                     clamped to [0, num_cols] (NULL: every column)
+ *   num_cols          0 <= num_cols <= DCP_TOPK_MAX_CANDIDATES
+ *   k                 1 <= k <= DCP_TOPK_MAX_CANDIDATES
+ *   out_scores        device, fp32, rows x k, row stride out_row_stride (>= k)
+ *   out_idx           device, int32, same layout as out_scores
+ *
+ * The two outputs must not overlap each other or an input (DCP_TOPK_EINVAL);
+ * rows == 0 returns DCP_TOPK_OK and enqueues nothing.
+ */
+DCP_TOPK_API int dcp_topk_local(const float* scores, int64_t score_row_stride, const int32_t* lengths,
+                   int32_t rows, int32_t num_cols, int32_t k, float* out_scores, int32_t* out_idx,
+                   int64_t out_row_stride, hipStream_t stream);
 
 /* Static, human-readable name of a status code. */
 DCP_TOPK_API const char* dcp_topk_status_string(int status);

@@ -22,6 +22,7 @@ from .build import INCLUDE, LIB_PATH
 OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP = 0, -1, -2, -3, -4
 MERGE_ROWS = 1024
 MAX_CANDIDATES = 16384
+FUSED_MAX_RANKS = 16
 WORKSPACE_ALIGN = 256
 
 _lib = None
@@ -54,6 +55,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.dcp_topk_merge_workspace_bytes.restype = sz
     lib.dcp_topk_merge_chunked.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, vp, sz, vp, vp]
     lib.dcp_topk_merge_chunked.restype = ctypes.c_int
+    lib.dcp_topk_merge_fused.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, vp, vp]
+    lib.dcp_topk_merge_fused.restype = ctypes.c_int
+    lib.dcp_topk_local.argtypes = [vp, i64, vp, i32, i32, i32, vp, vp, i64, vp]
+    lib.dcp_topk_local.restype = ctypes.c_int
     lib.dcp_topk_status_string.argtypes = [ctypes.c_int]
     lib.dcp_topk_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -90,6 +95,22 @@ def _require(t: torch.Tensor, name: str, dtype: torch.dtype, ndim: int) -> None:
         raise ValueError(f"{name} must be a device tensor")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
+
+
+def _require_rows(t: torch.Tensor, name: str, dtype: torch.dtype) -> None:
+    """A 2-D device tensor whose rows are contiguous (any row stride >= width)."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype or t.dim() != 2:
+        raise ValueError(f"{name} must be {dtype} with 2 dims, got {t.dtype} {tuple(t.shape)}")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device tensor")
+    if t.shape[1] > 1 and t.stride(1) != 1:
+        raise ValueError(f"{name} must have contiguous rows")
+
+
+def _row_stride(t: torch.Tensor) -> int:
+    return t.stride(0) if t.shape[0] > 1 else max(t.shape[1], 1)
 
 
 def candidates_from(scores: torch.Tensor, ids: torch.Tensor) -> torch.Tensor:
@@ -148,14 +169,7 @@ def merge_chunked(local_scores: Sequence[torch.Tensor], local_idx: Sequence[torc
     dcp = len(local_scores)
     if not (len(local_idx) == len(row_starts) == len(rank_offsets) == dcp) or dcp < 1:
         raise ValueError("one scores / idx / row_starts / offset per rank")
-    rows, local_k = local_scores[0].shape
-    for r in range(dcp):
-        _require(local_scores[r], f"local_scores[{r}]", torch.float32, 2)
-        _require(local_idx[r], f"local_idx[{r}]", torch.int32, 2)
-        _require(row_starts[r], f"row_starts[{r}]", torch.int32, 1)
-        if tuple(local_scores[r].shape) != (rows, local_k) or tuple(local_idx[r].shape) != (rows, local_k) \
-                or row_starts[r].shape[0] != rows:
-            raise ValueError("inconsistent shapes")
+    rows, local_k = _check_ranks(local_scores, local_idx, row_starts)
     device = local_scores[0].device
     need = merge_workspace_bytes(rows, dcp, local_k)
     if workspace is None:
@@ -164,17 +178,97 @@ def merge_chunked(local_scores: Sequence[torch.Tensor], local_idx: Sequence[torc
     if out is None:
         out = torch.empty((rows, k, 2), dtype=torch.int32, device=device)
     _require(out, "out", torch.int32, 3)
-    ptrs = ctypes.c_void_p * dcp
-    sp = ptrs(*[t.data_ptr() for t in local_scores])
-    ip = ptrs(*[t.data_ptr() for t in local_idx])
-    rp = ptrs(*[t.data_ptr() for t in row_starts])
-    offs = (ctypes.c_int32 * dcp)(*[int(x) for x in rank_offsets])
+    arrays = _RankArrays(local_scores, local_idx, row_starts, rank_offsets)  # alive for the call
+    sp, ip, rp, offs = arrays.args()
     _check("dcp_topk_merge_chunked",
-           lib.dcp_topk_merge_chunked(ctypes.cast(sp, ctypes.c_void_p), ctypes.cast(ip, ctypes.c_void_p),
-                                      ctypes.cast(rp, ctypes.c_void_p), ctypes.cast(offs, ctypes.c_void_p), dcp,
-                                      rows, local_k, int(k), _p(workspace.data_ptr()), workspace.numel(),
-                                      _p(out.data_ptr()), _stream(device)))
+           lib.dcp_topk_merge_chunked(sp, ip, rp, offs, dcp, rows, local_k, int(k), _p(workspace.data_ptr()),
+                                      workspace.numel(), _p(out.data_ptr()), _stream(device)))
     return out
+
+
+def _check_ranks(local_scores, local_idx, row_starts) -> tuple[int, int]:
+    dcp = len(local_scores)
+    if not (len(local_idx) == len(row_starts) == dcp) or dcp < 1:
+        raise ValueError("one scores / idx / row_starts / offset per rank")
+    rows, local_k = local_scores[0].shape
+    for r in range(dcp):
+        _require(local_scores[r], f"local_scores[{r}]", torch.float32, 2)
+        _require(local_idx[r], f"local_idx[{r}]", torch.int32, 2)
+        _require(row_starts[r], f"row_starts[{r}]", torch.int32, 1)
+        if tuple(local_scores[r].shape) != (rows, local_k) or tuple(local_idx[r].shape) != (rows, local_k) \
+                or row_starts[r].shape[0] != rows:
+            raise ValueError("inconsistent shapes")
+    return rows, local_k
+
+
+class _RankArrays:
+    """Host arrays of the ranks' device pointers, kept alive for one call."""
+
+    def __init__(self, local_scores, local_idx, row_starts, rank_offsets):
+        dcp = len(local_scores)
+        if len(rank_offsets) != dcp:
+            raise ValueError("one rank offset per rank")
+        ptrs = ctypes.c_void_p * dcp
+        self.sp = ptrs(*[t.data_ptr() for t in local_scores])
+        self.ip = ptrs(*[t.data_ptr() for t in local_idx])
+        self.rp = ptrs(*[t.data_ptr() for t in row_starts])
+        self.offs = (ctypes.c_int32 * dcp)(*[int(x) for x in rank_offsets])
+
+    def args(self):
+        return [ctypes.cast(a, ctypes.c_void_p) for a in (self.sp, self.ip, self.rp, self.offs)]
+
+
+def merge_fused(local_scores: Sequence[torch.Tensor], local_idx: Sequence[torch.Tensor],
+                row_starts: Sequence[torch.Tensor], rank_offsets: Sequence[int], k: int,
+                out: torch.Tensor | None = None) -> torch.Tensor:
+    """The merge without a gathered buffer: select straight from every rank's
+    local arrays (local_k a multiple of 64).  Same result as merge_chunked."""
+    lib = load_library()
+    rows, local_k = _check_ranks(local_scores, local_idx, row_starts)
+    device = local_scores[0].device
+    if out is None:
+        out = torch.empty((rows, k, 2), dtype=torch.int32, device=device)
+    _require(out, "out", torch.int32, 3)
+    if tuple(out.shape) != (rows, k, 2):
+        raise ValueError(f"out must be ({rows}, {k}, 2)")
+    arrays = _RankArrays(local_scores, local_idx, row_starts, rank_offsets)  # alive for the call
+    sp, ip, rp, offs = arrays.args()
+    _check("dcp_topk_merge_fused",
+           lib.dcp_topk_merge_fused(sp, ip, rp, offs, len(local_scores), rows, local_k, int(k),
+                                    _p(out.data_ptr()), _stream(device)))
+    return out
+
+
+def local_topk(scores: torch.Tensor, k: int, lengths: torch.Tensor | None = None,
+               out_scores: torch.Tensor | None = None, out_idx: torch.Tensor | None = None):
+    """Per row of ``scores`` (rows, num_cols) fp32 (rows contiguous, any row
+    stride): the k best of the first lengths[row] columns (all without
+    ``lengths``), ties to the lowest column, in column order, then (-inf, -1).
+    Returns (out_scores (rows, k) fp32, out_idx (rows, k) int32)."""
+    lib = load_library()
+    _require_rows(scores, "scores", torch.float32)
+    rows, num_cols = scores.shape
+    device = scores.device
+    if lengths is not None:
+        _require(lengths, "lengths", torch.int32, 1)
+        if lengths.shape[0] != rows:
+            raise ValueError("lengths must have one entry per row")
+    if out_scores is None:
+        out_scores = torch.empty((rows, k), dtype=torch.float32, device=device)
+    if out_idx is None:
+        out_idx = torch.empty((rows, k), dtype=torch.int32, device=device)
+    _require_rows(out_scores, "out_scores", torch.float32)
+    _require_rows(out_idx, "out_idx", torch.int32)
+    if tuple(out_scores.shape) != (rows, k) or tuple(out_idx.shape) != (rows, k):
+        raise ValueError(f"outputs must be ({rows}, {k})")
+    out_stride = _row_stride(out_scores)
+    if _row_stride(out_idx) != out_stride:
+        raise ValueError("out_scores and out_idx must share a row stride")
+    _check("dcp_topk_local",
+           lib.dcp_topk_local(_p(scores.data_ptr()), _row_stride(scores),
+                              _p(lengths.data_ptr() if lengths is not None else 0), rows, num_cols, int(k),
+                              _p(out_scores.data_ptr()), _p(out_idx.data_ptr()), out_stride, _stream(device)))
+    return out_scores, out_idx
 
 
 def split(cand: torch.Tensor):

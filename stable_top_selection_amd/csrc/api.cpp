@@ -48,7 +48,7 @@ int check_select(const dcp_topk_cand* cand, int32_t rows, int32_t num_cand, int3
   if (rows == 0) return DCP_TOPK_OK;
   if (out == nullptr || (num_cand > 0 && cand == nullptr)) return DCP_TOPK_EINVAL;
   if (!aligned(out, kCandBytes) || (cand != nullptr && !aligned(cand, kCandBytes))) return DCP_TOPK_EINVAL;
-  if (num_cand > DCP_TOPK_MAX_CANDIDATES) return DCP_TOPK_EUNSUPPORTED;
+  if (num_cand > DCP_TOPK_MAX_CANDIDATES || k > DCP_TOPK_MAX_CANDIDATES) return DCP_TOPK_EUNSUPPORTED;
   Span in_span, out_span;
   if (!strided_span(cand, rows, num_cand, num_cand, kCandBytes, &in_span)) return DCP_TOPK_EINVAL;
   if (!strided_span(out, rows, k, k, kCandBytes, &out_span)) return DCP_TOPK_EINVAL;
@@ -70,6 +70,26 @@ int check_pack(const float* scores, const int32_t* idx, int64_t src_row_stride, 
       !strided_span(dst, rows, local_k, dst_row_stride, kCandBytes, &d))
     return DCP_TOPK_EINVAL;
   if (overlap(d, s) || overlap(d, i) || overlap(d, r)) return DCP_TOPK_EINVAL;
+  return DCP_TOPK_OK;
+}
+
+// Rank r's local arrays (rows x local_k, contiguous rows) and row starts:
+// non-null, 4-byte aligned, disjoint from every span in `outputs`.
+int check_ranks(const float* const* local_scores, const int32_t* const* local_idx, const int32_t* const* row_starts,
+                int32_t dcp, int32_t rows, int32_t local_k, const Span* outputs, int n_outputs) {
+  for (int r = 0; r < dcp; ++r) {
+    const float* sc = local_scores[r];
+    const int32_t* ix = local_idx[r];
+    const int32_t* rs = row_starts[r];
+    if (sc == nullptr || ix == nullptr || rs == nullptr) return DCP_TOPK_EINVAL;
+    if (!aligned(sc, 4) || !aligned(ix, 4) || !aligned(rs, 4)) return DCP_TOPK_EINVAL;
+    Span s, i, rsp;
+    if (!strided_span(sc, rows, local_k, local_k, 4, &s) || !strided_span(ix, rows, local_k, local_k, 4, &i) ||
+        !strided_span(rs, rows, 1, 1, 4, &rsp))
+      return DCP_TOPK_EINVAL;
+    for (int o = 0; o < n_outputs; ++o)
+      if (overlap(outputs[o], s) || overlap(outputs[o], i) || overlap(outputs[o], rsp)) return DCP_TOPK_EINVAL;
+  }
   return DCP_TOPK_OK;
 }
 
@@ -123,7 +143,8 @@ int dcp_topk_merge_chunked(const float* const* local_scores, const int32_t* cons
   if (dcp < 1 || rows < 0 || local_k < 0 || k < 1) return DCP_TOPK_EINVAL;
   if (local_scores == nullptr || local_idx == nullptr || row_starts == nullptr || rank_offsets == nullptr)
     return DCP_TOPK_EINVAL;
-  if (static_cast<int64_t>(dcp) * local_k > DCP_TOPK_MAX_CANDIDATES) return DCP_TOPK_EUNSUPPORTED;
+  if (static_cast<int64_t>(dcp) * local_k > DCP_TOPK_MAX_CANDIDATES || k > DCP_TOPK_MAX_CANDIDATES)
+    return DCP_TOPK_EUNSUPPORTED;
   if (rows == 0) return DCP_TOPK_OK;
   const int32_t num_cand = dcp * local_k;
   const size_t need = dcp_topk_merge_workspace_bytes(rows, dcp, local_k);
@@ -136,18 +157,10 @@ int dcp_topk_merge_chunked(const float* const* local_scores, const int32_t* cons
   if (overlap(ws, o)) return DCP_TOPK_EINVAL;
   // The workspace holds one chunk (at most DCP_TOPK_MERGE_ROWS rows); the
   // inputs span all rows.
-  for (int r = 0; r < dcp && local_k > 0; ++r) {
-    const float* sc = local_scores[r];
-    const int32_t* ix = local_idx[r];
-    const int32_t* rs = row_starts[r];
-    if (sc == nullptr || ix == nullptr || rs == nullptr) return DCP_TOPK_EINVAL;
-    if (!aligned(sc, 4) || !aligned(ix, 4) || !aligned(rs, 4)) return DCP_TOPK_EINVAL;
-    Span s, i, rsp;
-    if (!strided_span(sc, rows, local_k, local_k, 4, &s) || !strided_span(ix, rows, local_k, local_k, 4, &i) ||
-        !strided_span(rs, rows, 1, 1, 4, &rsp))
-      return DCP_TOPK_EINVAL;
-    if (overlap(o, s) || overlap(o, i) || overlap(o, rsp) || overlap(ws, s) || overlap(ws, i) || overlap(ws, rsp))
-      return DCP_TOPK_EINVAL;
+  if (local_k > 0) {
+    const Span outputs[2] = {o, ws};
+    const int st = check_ranks(local_scores, local_idx, row_starts, dcp, rows, local_k, outputs, 2);
+    if (st != DCP_TOPK_OK) return st;
   }
 
   dcp_topk_cand* buf = static_cast<dcp_topk_cand*>(workspace);
@@ -170,6 +183,50 @@ int dcp_topk_merge_chunked(const float* const* local_scores, const int32_t* cons
     if (e != hipSuccess) return DCP_TOPK_EHIP;
   }
   return DCP_TOPK_OK;
+}
+
+int dcp_topk_merge_fused(const float* const* local_scores, const int32_t* const* local_idx,
+                         const int32_t* const* row_starts, const int32_t* rank_offsets, int32_t dcp, int32_t rows,
+                         int32_t local_k, int32_t k, dcp_topk_cand* out, hipStream_t stream) {
+  if (dcp < 1 || rows < 0 || local_k < 0 || k < 1) return DCP_TOPK_EINVAL;
+  if (local_scores == nullptr || local_idx == nullptr || row_starts == nullptr || rank_offsets == nullptr)
+    return DCP_TOPK_EINVAL;
+  if (dcp > dcptopk::kMaxFusedRanks || local_k % 64 != 0 ||
+      static_cast<int64_t>(dcp) * local_k > DCP_TOPK_MAX_CANDIDATES || k > DCP_TOPK_MAX_CANDIDATES)
+    return DCP_TOPK_EUNSUPPORTED;
+  if (rows == 0) return DCP_TOPK_OK;
+  if (out == nullptr || !aligned(out, kCandBytes)) return DCP_TOPK_EINVAL;
+  Span o;
+  if (!strided_span(out, rows, k, k, kCandBytes, &o)) return DCP_TOPK_EINVAL;
+  dcptopk::FusedRanks ranks{};
+  if (local_k > 0) {
+    const int st = check_ranks(local_scores, local_idx, row_starts, dcp, rows, local_k, &o, 1);
+    if (st != DCP_TOPK_OK) return st;
+    for (int r = 0; r < dcp; ++r) ranks.rank[r] = {local_scores[r], local_idx[r], row_starts[r], rank_offsets[r]};
+  }
+  return hip_status(dcptopk::launch_fused(ranks, local_k > 0 ? dcp : 0, rows, local_k, k, out, stream));
+}
+
+int dcp_topk_local(const float* scores, int64_t score_row_stride, const int32_t* lengths, int32_t rows,
+                   int32_t num_cols, int32_t k, float* out_scores, int32_t* out_idx, int64_t out_row_stride,
+                   hipStream_t stream) {
+  if (rows < 0 || num_cols < 0 || k < 1) return DCP_TOPK_EINVAL;
+  if (num_cols > DCP_TOPK_MAX_CANDIDATES || k > DCP_TOPK_MAX_CANDIDATES) return DCP_TOPK_EUNSUPPORTED;
+  if (rows == 0) return DCP_TOPK_OK;
+  if (out_scores == nullptr || out_idx == nullptr || (num_cols > 0 && scores == nullptr)) return DCP_TOPK_EINVAL;
+  if (score_row_stride < num_cols || out_row_stride < k) return DCP_TOPK_EINVAL;
+  if (!aligned(out_scores, 4) || !aligned(out_idx, 4) || (scores != nullptr && !aligned(scores, 4)) ||
+      (lengths != nullptr && !aligned(lengths, 4)))
+    return DCP_TOPK_EINVAL;
+  Span s, l, os, oi;
+  if (!strided_span(scores, rows, num_cols, score_row_stride, 4, &s) ||
+      !strided_span(lengths, lengths != nullptr ? rows : 0, 1, 1, 4, &l) ||
+      !strided_span(out_scores, rows, k, out_row_stride, 4, &os) ||
+      !strided_span(out_idx, rows, k, out_row_stride, 4, &oi))
+    return DCP_TOPK_EINVAL;
+  if (overlap(os, oi) || overlap(os, s) || overlap(os, l) || overlap(oi, s) || overlap(oi, l)) return DCP_TOPK_EINVAL;
+  return hip_status(dcptopk::launch_local(scores, score_row_stride, lengths, rows, num_cols, k, out_scores, out_idx,
+                                          out_row_stride, stream));
 }
 
 }  // extern "C"

@@ -25,6 +25,29 @@ struct PackRank {
 // Most ranks one pack launch handles; larger DCP groups take several launches.
 constexpr int kMaxPackRanks = 8;
 
+// Most ranks the fused merge reads in one launch (the ranks travel in the
+// kernel's arguments).
+constexpr int kMaxFusedRanks = DCP_TOPK_FUSED_MAX_RANKS;
+
+struct FusedRanks {
+  PackRank rank[kMaxFusedRanks];
+};
+
+// Enqueue the fused merge: select straight from the ranks' local arrays
+// (contiguous rows of local_k), as if they had been packed into a (rows,
+// dcp*local_k) buffer.  Arguments are already validated: 1 <= dcp <=
+// kMaxFusedRanks, local_k a multiple of 64, dcp*local_k <=
+// DCP_TOPK_MAX_CANDIDATES.
+hipError_t launch_fused(const FusedRanks& ranks, int32_t dcp, int32_t rows, int32_t local_k, int32_t k,
+                        dcp_topk_cand* out, hipStream_t stream);
+
+// Enqueue the local top-K: per row, the k best of the first lengths[row] (all
+// num_cols if lengths is null) columns, ids = columns, into separate score and
+// index arrays.  Arguments are already validated.
+hipError_t launch_local(const float* scores, int64_t score_row_stride, const int32_t* lengths, int32_t rows,
+                        int32_t num_cols, int32_t k, float* out_scores, int32_t* out_idx, int64_t out_row_stride,
+                        hipStream_t stream);
+
 // Enqueue the pack of `nranks` (<= kMaxPackRanks) ranks: rank r's row t goes to
 // dst + t*dst_row_stride + r*local_k.  Arguments are already validated.
 hipError_t launch_pack(const PackRank* ranks, int nranks, int64_t src_row_stride, int32_t rows,

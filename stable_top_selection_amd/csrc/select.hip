@@ -13,10 +13,17 @@
 // barrier after that.
 //
 // One workgroup (256 or 512 threads: 4 or 8 wave64s) owns one row.  Every
-// thread keeps N candidates in VGPRs for the whole kernel, at positions
-// v*VEC*BLOCK + VEC*t + j (chunk v < N/VEC, j < VEC), so the row is read from
-// HBM once, with 16-byte loads when VEC = 2 (each wave reads 1 KiB of
-// consecutive candidates per load instruction).
+// thread keeps N candidates in VGPRs for the whole kernel: wave w holds the
+// positions [w*64*N, (w+1)*64*N), its lane l the positions w*64*N +
+// v*64*VEC + VEC*l + j (chunk v < N/VEC, j < VEC), so the row is read from
+// memory once, each load instruction of a wave covering 64*VEC consecutive
+// candidates (16-byte loads when VEC = 2).
+//
+// Where the candidates come from and where the result goes are template
+// policies, so one selection core serves three entry points: a gathered
+// candidate buffer (the select), every DCP rank's local top-K arrays packed on
+// the fly (the fused merge), and a dense score row with the column as id (the
+// local top-K step, writing separate score and index arrays).
 //
 // Per row:
 //   1. key = bits ^ (negative ? 0xFFFFFFFF : 0x80000000), an order-preserving
@@ -37,10 +44,13 @@
 //      lowest positions win.
 //   5. Stable compaction: per-chunk selected counts packed 4 to a word, scanned
 //      across the wave with DPP and across waves through LDS (one barrier) in
-//      (chunk, wave, lane) order = candidate-position order.  Every item then
-//      issues one raw buffer store at its rank; unselected items store to an
-//      offset past the buffer's range, which the hardware drops, so the loop
-//      has no per-item branch.
+//      (wave, chunk, lane) order = candidate-position order.  A wave's selected
+//      items fill one contiguous output range; a wave stages them in LDS at
+//      their rank and writes the range with consecutive stores.  (A wave with
+//      more selected items than its staging area stores every item at its rank
+//      straight from registers; unselected items store to an offset past the
+//      buffer's range, which the hardware drops, so no loop has a per-item
+//      branch.)
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -57,6 +67,11 @@ constexpr uint32_t kBufferWord3 = 0x00020000u;  // raw buffer resource, gfx9 fam
 constexpr uint32_t kDropOffset = 0x80000000u;   // beyond any num_records used here
 
 typedef int int2v __attribute__((ext_vector_type(2)));
+
+// The padding candidate: what an empty output slot and an invalid local slot
+// hold.
+constexpr uint32_t kPadBits = 0xFF800000u;  // -inf
+constexpr uint32_t kPadId = 0x7FFFFFFFu;    // INT32_MAX
 
 // LDS-only workgroup barrier: waits for this wave's LDS traffic, not for its
 // outstanding global loads, so the row's loads stay in flight across it.
@@ -356,10 +371,238 @@ __device__ __forceinline__ void position_rank(const uint32_t (&flag)[N], uint32_
   }
 }
 
-template <int BLOCK, int VEC, int N, bool FULL>
-__global__ __launch_bounds__(BLOCK) void stable_topk_select_kernel(const dcp_topk_cand* __restrict__ cand,
-                                                                   int32_t num_cand, int32_t k,
-                                                                   dcp_topk_cand* __restrict__ out) {
+// ---------------------------------------------------------------------------
+// Candidate sources.  A source yields the (score bits, id) of this thread's
+// items: chunk v of wave w holds positions first + v*64*VEC + j (j < VEC), with
+// first = w*64*N + VEC*lane.  count(row) is the row's candidate count C (at
+// most the launch's num_cand); the values at positions at or past C are
+// ignored.  load() only issues the reads (into bits/idv and, for per-chunk
+// wave-uniform values, aux); finish() turns what arrived into (score bits, id)
+// after the kernel's first barrier, so that the loads stay in flight while the
+// kernel clears LDS.
+// ---------------------------------------------------------------------------
+
+// A row-major gathered candidate buffer: raw buffer loads over the row, the
+// chunk offset in a scalar register.
+struct GatheredSource {
+  const dcp_topk_cand* cand;
+  int32_t num_cand;
+
+  __device__ __forceinline__ int count(int64_t) const { return num_cand; }
+
+  template <int VEC, int NV>
+  __device__ __forceinline__ void finish(const uint32_t*, uint32_t*, uint32_t*) const {}
+
+  template <int VEC, int NV>
+  __device__ __forceinline__ void load(int64_t row, int first, int C, uint32_t* bits, uint32_t* idv,
+                                       uint32_t*) const {
+    constexpr int kChunk = VEC * kWave;
+    const __amdgpu_buffer_rsrc_t src = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<dcp_topk_cand*>(cand + row * num_cand), 0, C * static_cast<int>(sizeof(dcp_topk_cand)),
+        static_cast<int>(kBufferWord3));
+    const int voff = first * static_cast<int>(sizeof(dcp_topk_cand));
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+      const int soff = v * kChunk * static_cast<int>(sizeof(dcp_topk_cand));
+      if constexpr (VEC == 2) {
+        const int4 x = __builtin_bit_cast(int4, __builtin_amdgcn_raw_buffer_load_b128(src, voff, soff, 0));
+        bits[2 * v] = x.x;
+        idv[2 * v] = x.y;
+        bits[2 * v + 1] = x.z;
+        idv[2 * v + 1] = x.w;
+      } else {
+        const int2v x = __builtin_amdgcn_raw_buffer_load_b64(src, voff, soff, 0);
+        bits[v] = x.x;
+        idv[v] = x.y;
+      }
+    }
+  }
+};
+
+// Every DCP rank's local top-K arrays, read in place and packed on the fly
+// (the fused merge): position r*local_k + j of a row is rank r's slot j, its
+// id is local index + row start + rank offset with two's-complement wrap, and
+// a negative local index is the padding candidate (vLLM PR #59367, Purpose).
+// local_k is a multiple of 64*VEC, so a chunk never straddles two ranks and a
+// chunk's rank is wave-uniform.  A wave reads its chunks' rank-table entries
+// (scalar loads) before its first data load and the row starts (scalar loads
+// too) after its last, so that the data loads go out back to back and the
+// pack arithmetic waits only for its own operands.
+struct RankSource {
+  FusedRanks ranks;
+  int32_t local_k;
+  int32_t num_cand;  // dcp * local_k
+  int32_t last_rank;  // dcp - 1
+
+  __device__ __forceinline__ int count(int64_t) const { return num_cand; }
+
+  template <int VEC, int NV>
+  __device__ __forceinline__ void load(int64_t row, int first, int, uint32_t* bits, uint32_t* idv,
+                                       uint32_t* aux) const {
+    constexpr int kChunk = VEC * kWave;
+    const int lane_off = first & (kChunk - 1);
+    // the wave's first position, and the rank and local slot it falls in
+    const int chunk0 = __builtin_amdgcn_readfirstlane(first - lane_off);
+    int rk[NV], j0[NV];
+    {
+      int r = chunk0 / local_k;
+      int j = chunk0 - r * local_k;
+#pragma unroll
+      for (int v = 0; v < NV; ++v) {
+        // a chunk past the row (r > last_rank; its values are ignored) reads
+        // the last rank's slots instead, which are in bounds
+        rk[v] = r <= last_rank ? r : last_rank;
+        j0[v] = r <= last_rank ? j : 0;
+        j += kChunk;
+        if (j == local_k) {
+          j = 0;
+          ++r;
+        }
+      }
+    }
+    const float* sp[NV];
+    const int32_t* ip[NV];
+    const int32_t* rp[NV];
+    uint32_t off[NV];
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+      const PackRank& pr = ranks.rank[rk[v]];
+      sp[v] = pr.scores;
+      ip[v] = pr.idx;
+      rp[v] = pr.row_starts;
+      off[v] = static_cast<uint32_t>(pr.rank_offset);
+    }
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+      const int64_t at = row * local_k + j0[v] + lane_off;
+      if constexpr (VEC == 2) {
+        const uint2 s2 = *reinterpret_cast<const uint2*>(sp[v] + at);
+        const int2 i2 = *reinterpret_cast<const int2*>(ip[v] + at);
+        bits[2 * v] = s2.x;
+        bits[2 * v + 1] = s2.y;
+        idv[2 * v] = i2.x;
+        idv[2 * v + 1] = i2.y;
+      } else {
+        bits[v] = __builtin_bit_cast(uint32_t, sp[v][at]);
+        idv[v] = static_cast<uint32_t>(ip[v][at]);
+      }
+    }
+    // the id bases: scalar loads, counted apart from the vector loads, so
+    // waiting for them never waits for the data
+#pragma unroll
+    for (int v = 0; v < NV; ++v) aux[v] = static_cast<uint32_t>(rp[v][row]) + off[v];
+  }
+
+  // bits/idv hold score bits and local indices, aux the chunks' id bases
+  template <int VEC, int NV>
+  __device__ __forceinline__ void finish(const uint32_t* aux, uint32_t* bits, uint32_t* idv) const {
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+      const uint32_t base = aux[v];
+#pragma unroll
+      for (int j = 0; j < VEC; ++j) {
+        const bool invalid = static_cast<int32_t>(idv[v * VEC + j]) < 0;
+        bits[v * VEC + j] = invalid ? kPadBits : bits[v * VEC + j];
+        idv[v * VEC + j] = invalid ? kPadId : idv[v * VEC + j] + base;
+      }
+    }
+  }
+};
+
+// A dense fp32 score row (the local top-K step): the candidate at column c has
+// id c; with per-row lengths only the first lengths[row] columns take part.
+struct DenseSource {
+  const float* scores;
+  int64_t row_stride;
+  const int32_t* lengths;  // may be null
+  int32_t num_cols;
+
+  __device__ __forceinline__ int count(int64_t row) const {
+    if (lengths == nullptr) return num_cols;
+    const int len = lengths[row];
+    return len < 0 ? 0 : (len < num_cols ? len : num_cols);
+  }
+
+  template <int VEC, int NV>
+  __device__ __forceinline__ void finish(const uint32_t*, uint32_t*, uint32_t*) const {}
+
+  template <int VEC, int NV>
+  __device__ __forceinline__ void load(int64_t row, int first, int C, uint32_t* bits, uint32_t* idv,
+                                       uint32_t*) const {
+    constexpr int kChunk = VEC * kWave;
+    const __amdgpu_buffer_rsrc_t src = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float*>(scores + row * row_stride), 0, C * static_cast<int>(sizeof(float)),
+        static_cast<int>(kBufferWord3));
+    const int voff = first * static_cast<int>(sizeof(float));
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+      const int soff = v * kChunk * static_cast<int>(sizeof(float));
+      if constexpr (VEC == 2) {
+        const int2v x = __builtin_amdgcn_raw_buffer_load_b64(src, voff, soff, 0);
+        bits[2 * v] = x.x;
+        bits[2 * v + 1] = x.y;
+      } else {
+        bits[v] = __builtin_amdgcn_raw_buffer_load_b32(src, voff, soff, 0);
+      }
+#pragma unroll
+      for (int j = 0; j < VEC; ++j) idv[v * VEC + j] = static_cast<uint32_t>(first + v * kChunk + j);
+    }
+  }
+};
+
+// ---------------------------------------------------------------------------
+// Output sinks.  bind(row, k) gives the row's writer; store(keep, slot, bits,
+// id) writes one output slot (a store with keep == false is dropped by the
+// buffer range check), pad(slot) writes the padding candidate.
+// ---------------------------------------------------------------------------
+
+// (score bits, id) pairs, the candidate layout; padding is (-inf, INT32_MAX).
+struct PairSink {
+  dcp_topk_cand* out;
+  int64_t row_stride;
+
+  struct Row {
+    __amdgpu_buffer_rsrc_t r;
+    __device__ __forceinline__ void store(bool keep, uint32_t slot, uint32_t bits, uint32_t id) const {
+      const int2v data = {static_cast<int>(bits), static_cast<int>(id)};
+      __builtin_amdgcn_raw_buffer_store_b64(data, r, static_cast<int>(keep ? slot * 8u : kDropOffset), 0, 0);
+    }
+    __device__ __forceinline__ void pad(uint32_t slot) const { store(true, slot, kPadBits, kPadId); }
+  };
+
+  __device__ __forceinline__ Row bind(int64_t row, int k) const {
+    return Row{__builtin_amdgcn_make_buffer_rsrc(out + row * row_stride, 0, k * static_cast<int>(sizeof(dcp_topk_cand)),
+                                                 static_cast<int>(kBufferWord3))};
+  }
+};
+
+// Separate score and local-index arrays, the layout the pack step reads;
+// padding is (-inf, -1), which the pack turns into its padding candidate.
+struct SplitSink {
+  float* scores;
+  int32_t* idx;
+  int64_t row_stride;
+
+  struct Row {
+    __amdgpu_buffer_rsrc_t s, i;
+    __device__ __forceinline__ void store(bool keep, uint32_t slot, uint32_t bits, uint32_t id) const {
+      const int off = static_cast<int>(keep ? slot * 4u : kDropOffset);
+      __builtin_amdgcn_raw_buffer_store_b32(static_cast<int>(bits), s, off, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b32(static_cast<int>(id), i, off, 0, 0);
+    }
+    __device__ __forceinline__ void pad(uint32_t slot) const { store(true, slot, kPadBits, 0xFFFFFFFFu); }
+  };
+
+  __device__ __forceinline__ Row bind(int64_t row, int k) const {
+    return Row{__builtin_amdgcn_make_buffer_rsrc(scores + row * row_stride, 0, k * static_cast<int>(sizeof(float)),
+                                                 static_cast<int>(kBufferWord3)),
+               __builtin_amdgcn_make_buffer_rsrc(idx + row * row_stride, 0, k * static_cast<int>(sizeof(int32_t)),
+                                                 static_cast<int>(kBufferWord3))};
+  }
+};
+
+template <int BLOCK, int VEC, int N, bool FULL, class Source, class Sink>
+__global__ __launch_bounds__(BLOCK) void stable_topk_kernel(Source src, Sink sink, int32_t k) {
   static_assert(N <= 32 && N % VEC == 0, "flags are 32-bit masks");
   constexpr int NV = N / VEC;
   constexpr int kChunk = VEC * kWave;  // consecutive positions per chunk and wave
@@ -369,43 +612,37 @@ __global__ __launch_bounds__(BLOCK) void stable_topk_select_kernel(const dcp_top
   const int lane = t & (kWave - 1);
   const int w = __builtin_amdgcn_readfirstlane(t >> 6);
   const int64_t row = blockIdx.x;
-  const int C = num_cand;
-  const dcp_topk_cand* in = cand + row * C;
-  uint2* o = reinterpret_cast<uint2*>(out + row * static_cast<int64_t>(k));
+  const int C = src.count(row);
+  const typename Sink::Row dst = sink.bind(row, k);
+
+  // 1. issue every load of the row before touching LDS.  Wave w reads
+  // positions [w*64*N, (w+1)*64*N), 64*VEC consecutive ones per load.
+  const int first = w * kWave * N + VEC * lane;  // this thread's position in chunk 0
+  uint32_t bits[N], idv[N], aux[NV];
+  src.template load<VEC, NV>(row, first, C, bits, idv, aux);
+
+  // clear the histograms while the loads are in flight; the key transform
+  // stays after the barrier so that pass 0 starts on the first chunk while
+  // later chunks are still arriving
+  clear_words<BLOCK>(&lds.hist[0][0], 3 * kBins + 3 * kSmallBins, t);
+  lds_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+  src.template finish<VEC, NV>(aux, bits, idv);
 
   // k >= C: every candidate is selected, in place, then padding
   if (k >= C) {
-    const uint2* src = reinterpret_cast<const uint2*>(in);
-    for (int s = t; s < C; s += BLOCK) o[s] = src[s];
-    const uint2 pad = make_uint2(0xFF800000u, 0x7FFFFFFFu);
-    for (int s = C + t; s < k; s += BLOCK) o[s] = pad;
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+#pragma unroll
+      for (int j = 0; j < VEC; ++j) {
+        const int p = first + v * kChunk + j;
+        dst.store(p < C, static_cast<uint32_t>(p), bits[v * VEC + j], idv[v * VEC + j]);
+      }
+    }
+    for (int slot = C + t; slot < k; slot += BLOCK) dst.pad(static_cast<uint32_t>(slot));
     return;
   }
 
-  // 1. issue every load of the row before touching LDS: raw buffer loads over
-  // the row (positions past C read as zero and are masked out by `valid`); the
-  // chunk offset is a scalar, so a load costs no vector instruction.  Wave w
-  // reads positions [w*64*N, (w+1)*64*N), 1 KiB (VEC = 2) per load instruction.
-  const __amdgpu_buffer_rsrc_t src = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<dcp_topk_cand*>(in), 0, C * static_cast<int>(sizeof(dcp_topk_cand)), static_cast<int>(kBufferWord3));
-  const int first = w * kWave * N + VEC * lane;  // this thread's position in chunk 0
-  const int voff = first * static_cast<int>(sizeof(dcp_topk_cand));
-  uint32_t bits[N], idv[N];
-#pragma unroll
-  for (int v = 0; v < NV; ++v) {
-    const int soff = v * kChunk * static_cast<int>(sizeof(dcp_topk_cand));
-    if constexpr (VEC == 2) {
-      const int4 x = __builtin_bit_cast(int4, __builtin_amdgcn_raw_buffer_load_b128(src, voff, soff, 0));
-      bits[2 * v] = x.x;
-      idv[2 * v] = x.y;
-      bits[2 * v + 1] = x.z;
-      idv[2 * v + 1] = x.w;
-    } else {
-      const int2v x = __builtin_amdgcn_raw_buffer_load_b64(src, voff, soff, 0);
-      bits[v] = x.x;
-      idv[v] = x.y;
-    }
-  }
   // FULL: the row fills every slot (C == BLOCK*N); else the last are masked out
   uint32_t valid = 0xFFFFFFFFu >> (32 - N);
   if constexpr (!FULL) {
@@ -416,12 +653,6 @@ __global__ __launch_bounds__(BLOCK) void stable_topk_select_kernel(const dcp_top
       for (int j = 0; j < VEC; ++j) valid |= (first + v * kChunk + j < C) ? 1u << (v * VEC + j) : 0u;
   }
 
-  // clear the histograms while the loads are in flight; the key transform
-  // stays after the barrier so that pass 0 starts on the first chunk while
-  // later chunks are still arriving
-  clear_words<BLOCK>(&lds.hist[0][0], 3 * kBins + 3 * kSmallBins, t);
-  lds_barrier();
-  __builtin_amdgcn_sched_barrier(0);
   uint32_t key[N];
 #pragma unroll
   for (int i = 0; i < N; ++i) key[i] = score_key(bits[i]);
@@ -555,8 +786,6 @@ __global__ __launch_bounds__(BLOCK) void stable_topk_select_kernel(const dcp_top
   // spare slot, so the staging loop has no per-item branch.
   uint32_t rank[N], out_first, out_count;
   position_rank<BLOCK, VEC, N>(sel, lds.segment[1], rank, lane, w, &out_first, &out_count);
-  const __amdgpu_buffer_rsrc_t dst = __builtin_amdgcn_make_buffer_rsrc(o, 0, k * static_cast<int>(sizeof(uint2)),
-                                                                        static_cast<int>(kBufferWord3));
   // items a wave can stage: half of its slots, at most 512 (a wave past that
   // stores straight from registers)
   constexpr int kStageCap = kWave * N / 2 < 512 ? kWave * N / 2 : 512;
@@ -573,51 +802,79 @@ __global__ __launch_bounds__(BLOCK) void stable_topk_select_kernel(const dcp_top
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
     for (uint32_t e = lane; e < out_count; e += kWave) {
       const uint2 x = stage[e];
-      const int2v data = {static_cast<int>(x.x), static_cast<int>(x.y)};
-      __builtin_amdgcn_raw_buffer_store_b64(data, dst, static_cast<int>((out_first + e) * 8u), 0, 0);
+      dst.store(true, out_first + e, x.x, x.y);
     }
   } else {
 #pragma unroll
     for (int i = 0; i < N; ++i) {
-      const uint32_t off = sel[i] ? rank[i] * 8u : kDropOffset;
-      const int2v data = {static_cast<int>(bits[i]), static_cast<int>(idv[i])};
-      __builtin_amdgcn_raw_buffer_store_b64(data, dst, static_cast<int>(off), 0, 0);
+      dst.store(sel[i] != 0u, rank[i], bits[i], idv[i]);
     }
   }
 }
 
-template <int BLOCK, int VEC, int N>
-hipError_t launch(const dcp_topk_cand* cand, int32_t rows, int32_t num_cand, int32_t k, dcp_topk_cand* out,
+// full: every row has exactly BLOCK*N candidates, so no item is masked out
+template <int BLOCK, int VEC, int N, class Source, class Sink>
+hipError_t launch(const Source& src, const Sink& sink, bool uniform_rows, int32_t rows, int32_t num_cand, int32_t k,
                   hipStream_t stream) {
-  void* args[] = {const_cast<dcp_topk_cand**>(&cand), &num_cand, &k, &out};
-  const void* fn = num_cand == BLOCK * N
-                       ? reinterpret_cast<const void*>(&stable_topk_select_kernel<BLOCK, VEC, N, true>)
-                       : reinterpret_cast<const void*>(&stable_topk_select_kernel<BLOCK, VEC, N, false>);
+  Source a = src;
+  Sink b = sink;
+  void* args[] = {&a, &b, &k};
+  const void* fn = uniform_rows && num_cand == BLOCK * N
+                       ? reinterpret_cast<const void*>(&stable_topk_kernel<BLOCK, VEC, N, true, Source, Sink>)
+                       : reinterpret_cast<const void*>(&stable_topk_kernel<BLOCK, VEC, N, false, Source, Sink>);
   return hipLaunchKernel(fn, dim3(rows), dim3(BLOCK), args, 0, stream);
+}
+
+// 256 threads up to 2048 candidates, 512 above; the smallest item count per
+// thread that covers the row.
+template <int VEC, class Source, class Sink>
+hipError_t launch_sized(const Source& src, const Sink& sink, bool uniform_rows, int32_t rows, int32_t num_cand,
+                        int32_t k, hipStream_t stream) {
+  constexpr int kSmall = 256 * VEC;  // positions covered by 256 threads with one chunk
+  const bool u = uniform_rows;
+  if (num_cand <= kSmall) return launch<256, VEC, VEC>(src, sink, u, rows, num_cand, k, stream);
+  if (num_cand <= 2 * kSmall) return launch<256, VEC, 2 * VEC>(src, sink, u, rows, num_cand, k, stream);
+  if (num_cand <= 4 * kSmall) return launch<256, VEC, 4 * VEC>(src, sink, u, rows, num_cand, k, stream);
+  if (num_cand <= 2048) return launch<256, VEC, 8>(src, sink, u, rows, num_cand, k, stream);
+  if (num_cand <= 4096) return launch<512, VEC, 8>(src, sink, u, rows, num_cand, k, stream);
+  if (num_cand <= 8192) return launch<512, VEC, 16>(src, sink, u, rows, num_cand, k, stream);
+  return launch<512, VEC, 32>(src, sink, u, rows, num_cand, k, stream);
 }
 
 }  // namespace
 
 hipError_t launch_select(const dcp_topk_cand* cand, int32_t rows, int32_t num_cand, int32_t k, dcp_topk_cand* out,
                          hipStream_t stream) {
-  // 256 threads up to 2048 candidates, 512 above; the smallest item count per
-  // thread that covers the row.
-  const bool vec2 = (num_cand % 2 == 0) && (reinterpret_cast<uintptr_t>(cand) % 16 == 0);
-  if (vec2) {
-    if (num_cand <= 512) return launch<256, 2, 2>(cand, rows, num_cand, k, out, stream);
-    if (num_cand <= 1024) return launch<256, 2, 4>(cand, rows, num_cand, k, out, stream);
-    if (num_cand <= 2048) return launch<256, 2, 8>(cand, rows, num_cand, k, out, stream);
-    if (num_cand <= 4096) return launch<512, 2, 8>(cand, rows, num_cand, k, out, stream);
-    if (num_cand <= 8192) return launch<512, 2, 16>(cand, rows, num_cand, k, out, stream);
-    return launch<512, 2, 32>(cand, rows, num_cand, k, out, stream);
-  }
-  if (num_cand <= 256) return launch<256, 1, 1>(cand, rows, num_cand, k, out, stream);
-  if (num_cand <= 512) return launch<256, 1, 2>(cand, rows, num_cand, k, out, stream);
-  if (num_cand <= 1024) return launch<256, 1, 4>(cand, rows, num_cand, k, out, stream);
-  if (num_cand <= 2048) return launch<256, 1, 8>(cand, rows, num_cand, k, out, stream);
-  if (num_cand <= 4096) return launch<512, 1, 8>(cand, rows, num_cand, k, out, stream);
-  if (num_cand <= 8192) return launch<512, 1, 16>(cand, rows, num_cand, k, out, stream);
-  return launch<512, 1, 32>(cand, rows, num_cand, k, out, stream);
+  const GatheredSource src{cand, num_cand};
+  const PairSink sink{out, k};
+  if ((num_cand % 2 == 0) && (reinterpret_cast<uintptr_t>(cand) % 16 == 0))
+    return launch_sized<2>(src, sink, true, rows, num_cand, k, stream);
+  return launch_sized<1>(src, sink, true, rows, num_cand, k, stream);
+}
+
+hipError_t launch_fused(const FusedRanks& ranks, int32_t dcp, int32_t rows, int32_t local_k, int32_t k,
+                        dcp_topk_cand* out, hipStream_t stream) {
+  const PairSink sink{out, k};
+  if (dcp * local_k == 0)  // no candidates: every slot is padding, nothing is read
+    return launch_sized<1>(GatheredSource{nullptr, 0}, sink, true, rows, 0, k, stream);
+  const RankSource src{ranks, local_k, dcp * local_k, dcp - 1};
+  bool pairs = local_k % (2 * kWave) == 0;
+  for (int r = 0; r < dcp; ++r)
+    pairs = pairs && reinterpret_cast<uintptr_t>(ranks.rank[r].scores) % 8 == 0 &&
+            reinterpret_cast<uintptr_t>(ranks.rank[r].idx) % 8 == 0;
+  if (pairs) return launch_sized<2>(src, sink, true, rows, dcp * local_k, k, stream);
+  return launch_sized<1>(src, sink, true, rows, dcp * local_k, k, stream);
+}
+
+hipError_t launch_local(const float* scores, int64_t score_row_stride, const int32_t* lengths, int32_t rows,
+                        int32_t num_cols, int32_t k, float* out_scores, int32_t* out_idx, int64_t out_row_stride,
+                        hipStream_t stream) {
+  const DenseSource src{scores, score_row_stride, lengths, num_cols};
+  const SplitSink sink{out_scores, out_idx, out_row_stride};
+  const bool uniform_rows = lengths == nullptr;
+  if ((num_cols % 2 == 0) && (score_row_stride % 2 == 0) && (reinterpret_cast<uintptr_t>(scores) % 8 == 0))
+    return launch_sized<2>(src, sink, uniform_rows, rows, num_cols, k, stream);
+  return launch_sized<1>(src, sink, uniform_rows, rows, num_cols, k, stream);
 }
 
 }  // namespace dcptopk

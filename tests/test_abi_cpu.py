@@ -24,7 +24,8 @@ def lib():
 def test_exports_every_header_function(lib):
     names = B.header_functions()
     assert set(names) == {"dcp_topk_pack", "dcp_topk_select", "dcp_topk_merge_workspace_bytes",
-                          "dcp_topk_merge_chunked", "dcp_topk_status_string"}
+                          "dcp_topk_merge_chunked", "dcp_topk_merge_fused", "dcp_topk_local",
+                          "dcp_topk_status_string"}
     for n in names:
         assert hasattr(lib, n), n
     exported = subprocess.run(["nm", "-D", "--defined-only", LIB_PATH], capture_output=True, text=True).stdout
@@ -59,6 +60,7 @@ def test_select_argument_checks(lib):
     assert s(P(DEV_A + 4), 1, 64, 1, P(DEV_B), None) == B.EINVAL  # misaligned input
     assert s(P(DEV_A), 1, 64, 1, P(DEV_B + 2), None) == B.EINVAL  # misaligned output
     assert s(P(DEV_A), 1, 16385, 1, P(DEV_B), None) == B.EUNSUPPORTED
+    assert s(P(DEV_A), 1, 64, 16385, P(DEV_B), None) == B.EUNSUPPORTED  # k past the limit
     # output overlapping the input: row 1 of the input is the output
     assert s(P(DEV_A), 4, 64, 16, P(DEV_A + 64 * 8), None) == B.EINVAL
 
@@ -99,3 +101,60 @@ def test_merge_argument_checks(lib):
     assert m(*args(DEV_A + 0x4000000, ws_need, DEV_B)) == B.EINVAL  # workspace overlaps row starts
     assert m(None, cast(ix), cast(rs), cast(offs), 2, 64, 128, 64, P(DEV_B), ws_need, P(DEV_B + 0x1000000),
              None) == B.EINVAL
+
+
+def _rank_arrays(n, base=DEV_A):
+    arr = ctypes.c_void_p * n
+    sc = arr(*[base + r * 0x1000000 for r in range(n)])
+    ix = arr(*[base + 0x40000000 + r * 0x1000000 for r in range(n)])
+    rs = arr(*[base + 0x80000000 + r * 0x1000000 for r in range(n)])
+    offs = (ctypes.c_int32 * n)(*[r * 1000 for r in range(n)])
+    return [ctypes.cast(x, P) for x in (sc, ix, rs, offs)]
+
+
+def test_merge_fused_argument_checks(lib):
+    f = lib.dcp_topk_merge_fused
+    ok = _rank_arrays(2)
+    args = lambda out, dcp=2, rows=64, lk=128, k=64, ranks=ok: (*ranks, dcp, rows, lk, k, P(out), None)  # noqa: E731
+    assert f(*args(DEV_B, rows=0)) == B.OK
+    assert f(*args(DEV_B, dcp=0)) == B.EINVAL
+    assert f(*args(DEV_B, k=0)) == B.EINVAL
+    assert f(*args(DEV_B, rows=-1)) == B.EINVAL
+    assert f(*args(DEV_B, lk=100)) == B.EUNSUPPORTED  # local_k not a multiple of 64
+    assert f(*args(DEV_B, k=16385)) == B.EUNSUPPORTED
+    many = _rank_arrays(17)
+    assert f(*args(DEV_B, dcp=17, ranks=many)) == B.EUNSUPPORTED
+    three = _rank_arrays(3)
+    assert f(*args(DEV_B, dcp=3, lk=8192, ranks=three)) == B.EUNSUPPORTED  # 24576 candidates
+    assert f(*args(None)) == B.EINVAL
+    assert f(*args(DEV_B + 4)) == B.EINVAL  # output not 8-byte aligned
+    assert f(*args(DEV_A + 0x40000000)) == B.EINVAL  # output overlaps rank 0's indices
+    assert f(*args(DEV_A + 0x81000000)) == B.EINVAL  # output overlaps rank 1's row starts
+    null_rank = _rank_arrays(2)
+    ctypes.cast(null_rank[0], ctypes.POINTER(ctypes.c_void_p))[1] = None
+    assert f(*args(DEV_B, ranks=null_rank)) == B.EINVAL
+    assert f(None, ok[1], ok[2], ok[3], 2, 64, 128, 64, P(DEV_B), None) == B.EINVAL
+
+
+def test_local_argument_checks(lib):
+    loc = lib.dcp_topk_local
+    a, lens, os_, oi = DEV_A, DEV_A + 0x1000000, DEV_B, DEV_B + 0x1000000
+    args = lambda s=a, stride=4096, ln=None, rows=64, cols=4096, k=2048, o1=os_, o2=oi, ostride=2048: (  # noqa: E731
+        P(s), stride, P(ln), rows, cols, k, P(o1), P(o2), ostride, None)
+    assert loc(*args(rows=0)) == B.OK
+    assert loc(*args(rows=-1)) == B.EINVAL
+    assert loc(*args(k=0)) == B.EINVAL
+    assert loc(*args(cols=-1)) == B.EINVAL
+    assert loc(*args(cols=16385, stride=16385)) == B.EUNSUPPORTED
+    assert loc(*args(k=16385, ostride=16385)) == B.EUNSUPPORTED
+    assert loc(*args(s=None)) == B.EINVAL
+    assert loc(*args(o1=None)) == B.EINVAL
+    assert loc(*args(o2=None)) == B.EINVAL
+    assert loc(*args(stride=4095)) == B.EINVAL  # row stride narrower than the row
+    assert loc(*args(ostride=2047)) == B.EINVAL
+    assert loc(*args(s=a + 2)) == B.EINVAL  # misaligned scores
+    assert loc(*args(o2=oi + 1)) == B.EINVAL  # misaligned index output
+    assert loc(*args(ln=lens + 2)) == B.EINVAL  # misaligned lengths
+    assert loc(*args(o2=os_ + 4)) == B.EINVAL  # the two outputs overlap
+    assert loc(*args(o1=a + 4096 * 4)) == B.EINVAL  # score output inside the scores
+    assert loc(*args(ln=oi + 64)) == B.EINVAL  # lengths inside the index output

@@ -1,0 +1,195 @@
+"""GPU parity of dcp_topk_merge_fused (the merge that reads every rank's local
+arrays in place) with the CPU oracle's merge."""
+import numpy as np
+import pytest
+import torch
+
+from gpu_helpers import DEV, to_dev
+from oracle import stable_topk as O
+from stable_top_selection_amd import binding as B
+from stable_top_selection_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+INT32_MAX = 2**31 - 1
+PAD_BITS = 0xFF800000
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    B.load_library()
+
+
+def _dev_shards(sh, misalign=False):
+    """Device copies of the shards; ``misalign`` starts every score and index
+    array 4 bytes past an 8-byte boundary (the 4-byte load path)."""
+    def put(a):
+        if not misalign:
+            return to_dev(a)
+        flat = torch.zeros(a.size + 1, dtype=torch.from_numpy(a).dtype, device=DEV)
+        flat[1:] = to_dev(a.reshape(-1))
+        t = flat[1:].view(a.shape)
+        assert t.data_ptr() % 8 == 4
+        return t
+
+    return ([put(sh.scores[r]) for r in range(sh.dcp)], [put(sh.local_idx[r]) for r in range(sh.dcp)],
+            [to_dev(sh.row_starts[r]) for r in range(sh.dcp)], [int(x) for x in sh.rank_offsets])
+
+
+def _random_shards(rows, dcp, local_k, seed, invalid_frac=0.0, span=4096, dist="normal"):
+    rng = np.random.default_rng(seed)
+    if dist == "levels":
+        scores = W.TIE_LEVELS[rng.integers(0, 16, size=(dcp, rows, local_k))]
+    else:
+        scores = rng.standard_normal((dcp, rows, local_k), dtype=np.float32)
+    span = max(span, local_k)
+    idx = np.stack([W.distinct_per_row(rng, rows, local_k, span) for _ in range(dcp)]) if local_k else \
+        np.zeros((dcp, rows, 0), np.int32)
+    if invalid_frac:
+        idx = np.where(rng.random(idx.shape) < invalid_frac, np.int32(-1), idx).astype(np.int32)
+    starts = rng.integers(0, 131072, size=(dcp, rows), dtype=np.int32)
+    offs = (np.arange(dcp) * (131072 + span)).astype(np.int32)
+    return W.LocalShards("random", np.ascontiguousarray(scores), idx, starts, offs, k=0)
+
+
+def _fused(sh, k, guard=2, misalign=False):
+    """Fused merge on the GPU with canary rows around the output; returns the
+    output as numpy (rows, k, 2)."""
+    sc, ix, rs, offs = _dev_shards(sh, misalign)
+    canary = torch.tensor([0x5EED5EED, 0x0BADF00D], dtype=torch.int32, device=DEV)
+    big = canary.repeat((sh.rows + 2 * guard) * k).view(sh.rows + 2 * guard, k, 2)
+    out = big[guard:guard + sh.rows]
+    B.merge_fused(sc, ix, rs, offs, k, out=out)
+    torch.cuda.synchronize()
+    g = big.cpu().numpy()
+    for part in (g[:guard], g[guard + sh.rows:]):
+        assert np.all(part[..., 0] == 0x5EED5EED) and np.all(part[..., 1] == 0x0BADF00D), "wrote outside out"
+    return g[guard:guard + sh.rows]
+
+
+def _assert_rows(o, want_s, want_i, rows, label):
+    ob = o[..., 0].view(np.uint32)
+    ok = (ob[rows] == want_s.view(np.uint32)).all(1) & (o[rows, :, 1] == want_i).all(1)
+    assert ok.all(), f"{label}: {np.count_nonzero(~ok)} rows differ, first {np.asarray(rows)[~ok][0]}"
+
+
+def _parity(sh, k, label, **kw):
+    print(f"[fused parity] {label}", flush=True)
+    o = _fused(sh, k, **kw)
+    want_s, want_i = O.merge(sh.scores, sh.local_idx, sh.row_starts, sh.rank_offsets, k)
+    _assert_rows(o, want_s, want_i, np.arange(sh.rows), label)
+
+
+def test_fused_large_shape():
+    """256 rows of DCP 4 x local K 2048 = 8192 candidates, K 2048."""
+    sh = W.fused()
+    _parity(sh, sh.k, f"{sh.name} digest={sh.digest()}")
+
+
+@pytest.mark.parametrize("rows", [1, 5, 16, 64, 1025])
+def test_fused_prefill_shape(rows):
+    sh = W.prefill(rows=rows, seed=60 + rows, invalid_frac=0.02)
+    _parity(sh, 2048, f"prefill T={rows} invalid 2% digest={sh.digest()}")
+
+
+def test_fused_full_prefill_sampled():
+    """All T = 8192 prefill rows in one launch: 96 sampled rows against the
+    oracle, and every row against the chunked merge (itself checked against the
+    oracle on every row of this workload)."""
+    sh = W.prefill()
+    print(f"[fused parity] {sh.name} digest={sh.digest()}", flush=True)
+    o = _fused(sh, sh.k, guard=1)
+    rows = np.sort(np.random.default_rng(8192).choice(sh.rows, 96, replace=False))
+    rows[0], rows[-1] = 0, sh.rows - 1
+    want_s, want_i = O.merge(sh.scores[:, rows], sh.local_idx[:, rows], sh.row_starts[:, rows],
+                             sh.rank_offsets, sh.k)
+    _assert_rows(o, want_s, want_i, rows, "full prefill, sampled rows")
+    sc, ix, rs, offs = _dev_shards(sh)
+    chunked = B.merge_chunked(sc, ix, rs, offs, sh.k)
+    torch.cuda.synchronize()
+    assert np.array_equal(chunked.cpu().numpy(), o)
+
+
+@pytest.mark.parametrize("rows,dcp,local_k,k,dist", [
+    (37, 3, 128, 50, "normal"), (20, 9, 64, 100, "normal"), (11, 2, 192, 20, "levels"),
+    (300, 4, 64, 1, "normal"), (6, 16, 1024, 2048, "normal"), (9, 1, 4096, 4095, "levels"),
+    (7, 4, 4096, 2048, "levels"), (5, 2, 8192, 3000, "normal"), (13, 5, 320, 2000, "levels"),
+    (3, 4, 64, 300, "normal"), (8, 8, 256, 257, "levels")])
+def test_fused_ragged(rows, dcp, local_k, k, dist):
+    sh = _random_shards(rows, dcp, local_k, seed=rows * dcp + local_k + k, invalid_frac=0.1, dist=dist)
+    _parity(sh, k, f"ragged rows={rows} dcp={dcp} local_k={local_k} k={k} {dist}")
+
+
+@pytest.mark.parametrize("local_k", [128, 192, 2048])
+def test_fused_4_byte_aligned_inputs(local_k):
+    """Score and index arrays 4 bytes past an 8-byte boundary take the 4-byte
+    load path."""
+    sh = _random_shards(9, 4, local_k, seed=local_k, invalid_frac=0.05)
+    _parity(sh, 200, f"misaligned local_k={local_k}", misalign=True)
+
+
+def test_fused_empty_shard_and_no_candidates():
+    """A rank whose slots are all invalid packs to padding; local_k = 0 pads
+    every output slot."""
+    sh = _random_shards(8, 4, 512, seed=3)
+    sh.local_idx[2, ::2] = -1  # rank 2 is an empty shard in even rows
+    _parity(sh, 1800, "empty shard")
+    empty = _random_shards(3, 4, 0, seed=4)
+    o = _fused(empty, 5)
+    assert np.all(o[..., 0].view(np.uint32) == PAD_BITS) and np.all(o[..., 1] == INT32_MAX)
+
+
+def test_fused_equals_chunked_on_ties():
+    """Tie-heavy scores with repeated global ids across ranks (rank offsets 0):
+    the fused merge and the chunked merge agree bit for bit."""
+    sh = _random_shards(40, 4, 2048, seed=5, dist="levels", invalid_frac=0.05)
+    sh.rank_offsets[:] = 0
+    sh.row_starts[:] = sh.row_starts[0]
+    sc, ix, rs, offs = _dev_shards(sh)
+    a = B.merge_fused(sc, ix, rs, offs, 2048)
+    b = B.merge_chunked(sc, ix, rs, offs, 2048)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+    _parity(sh, 2048, "ties with shared ids")
+
+
+def test_fused_graph_replay():
+    """Captured into a HIP graph and replayed three times, with eager work and
+    a synchronisation between replays: every replay matches the oracle."""
+    sh = W.prefill(rows=64, seed=77)
+    sc, ix, rs, offs = _dev_shards(sh)
+    out = torch.empty((64, 2048, 2), dtype=torch.int32, device=DEV)
+    B.merge_fused(sc, ix, rs, offs, 2048, out=out)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        B.merge_fused(sc, ix, rs, offs, 2048, out=out)
+    want_s, want_i = O.merge(sh.scores, sh.local_idx, sh.row_starts, sh.rank_offsets, 2048)
+    for rep in range(3):
+        out.fill_(0)
+        g.replay()
+        torch.cuda.synchronize()
+        _assert_rows(out.cpu().numpy(), want_s, want_i, np.arange(64), f"graph replay {rep}")
+
+
+def test_fused_unsupported_and_invalid():
+    sh = _random_shards(4, 2, 100, seed=6)
+    sc, ix, rs, offs = _dev_shards(sh)
+    with pytest.raises(B.DcpTopkError) as e:  # local_k not a multiple of 64
+        B.merge_fused(sc, ix, rs, offs, 10)
+    assert e.value.status == B.EUNSUPPORTED
+    many = _random_shards(2, 17, 64, seed=7)
+    with pytest.raises(B.DcpTopkError) as e:  # more ranks than one launch takes
+        B.merge_fused(*_dev_shards(many), 10)
+    assert e.value.status == B.EUNSUPPORTED
+    wide = _random_shards(1, 3, 8192, seed=8)
+    with pytest.raises(B.DcpTopkError) as e:  # 24576 candidates per row
+        B.merge_fused(*_dev_shards(wide), 10)
+    assert e.value.status == B.EUNSUPPORTED
+    ok = _random_shards(4, 2, 64, seed=9)
+    sc, ix, rs, offs = _dev_shards(ok)
+    alias = sc[0].view(torch.int32).view(4, 32, 2)
+    with pytest.raises(B.DcpTopkError) as e:  # output overlaps rank 0's scores
+        B.merge_fused(sc, ix, rs, offs, 32, out=alias)
+    assert e.value.status == B.EINVAL
