@@ -63,6 +63,7 @@ constexpr int kWave = 64;
 constexpr int kBins = 2048;      // widest digit: 11 bits
 constexpr int kSmallBins = 256;  // list passes: digits of at most 8 bits
 constexpr int kListCap = 2048;   // largest threshold bucket handled as a list
+constexpr int kFew = 16;         // threshold sub-bins this small are resolved by comparison
 constexpr uint32_t kBufferWord3 = 0x00020000u;  // raw buffer resource, gfx9 family
 constexpr uint32_t kDropOffset = 0x80000000u;   // beyond any num_records used here
 
@@ -221,10 +222,14 @@ struct alignas(16) SelectLds {
   static constexpr int kWaves = BLOCK / kWave;
   uint32_t hist[3][kBins];         // pass 0 (hist[0]) and the register passes, rotating
   uint32_t small[3][kSmallBins];   // list passes, rotating
-  uint2 list[kListCap];            // (key, id) of the items in the pass-0 threshold bin
+  uint2 list[kListCap + kWave];    // (key, id) of the items in the pass-0 threshold bin, then
+                                   // one write-only dump slot per lane
   uint32_t segment[2][kWaves];     // per-wave flagged counts (dup scan, select scan)
   uint32_t sink[kWave];            // per-lane target of atomics whose item does not count
   uint32_t common[8];              // OR / AND of list keys and ids, per wave pair
+  uint2 few[kFew];                 // (key, ~id) of the items of a small threshold sub-bin
+  uint32_t few_count;              // items gathered into few (zeroed at start)
+  uint32_t pad_[3];
 };
 
 // Clear `words` (a multiple of 4) words of LDS.
@@ -258,8 +263,8 @@ __device__ __forceinline__ void radix_pass(SelectLds<BLOCK>& lds, int pass, cons
 // List pass q over the digit at SHIFT (BITS wide): score keys of the list
 // (BY_ID false) or complemented ids of the list items whose key is `thr`.
 // Uses small[q % 3]; after its barrier clears small[(q + 2) % 3], which pass
-// q - 1 used and pass q + 2 will use.  Pass 0 of the score keys is counted
-// while the list is built, so this starts at pass 1.
+// q - 1 used and pass q + 2 will use.  Pass 0 (the 8 key bits below the
+// first 11) runs right after the list is built.
 template <int BLOCK, int SHIFT, int BITS, bool BY_ID>
 __device__ __forceinline__ void list_pass(SelectLds<BLOCK>& lds, int q, int m, uint32_t thr, Radix& st, int t,
                                           int lane) {
@@ -274,6 +279,62 @@ __device__ __forceinline__ void list_pass(SelectLds<BLOCK>& lds, int q, int m, u
   lds_barrier();
   if (t < kSmallBins / 4) *reinterpret_cast<uint4*>(lds.small[(q + 2) % 3] + 4 * t) = make_uint4(0u, 0u, 0u, 0u);
   advance(st, find_digit_small<NB>(hist, st.need, lane), SHIFT, kDigitMask);
+}
+
+// A threshold sub-bin of at most kFew items (sk.count of them match sk's
+// prefix) is finished by comparison instead of histogram passes: its items'
+// (key, ~id) pairs are gathered from the list into lds.few, and after one
+// barrier every wave ranks them directly.  Gather at most
+// once per row (lds.few_count is zeroed only at the start).
+__device__ __forceinline__ void few_put(uint32_t* count, uint2* few, uint32_t key, uint32_t id) {
+  const uint32_t slot = lds_add(count);
+  if (slot < static_cast<uint32_t>(kFew)) few[slot] = make_uint2(key, ~id);
+}
+
+template <int BLOCK>
+__device__ __forceinline__ void few_gather_list(SelectLds<BLOCK>& lds, int m, const Radix& sk, int t) {
+  for (int e = t; e < m; e += BLOCK) {
+    const uint2 x = lds.list[e];
+    if ((x.x & sk.mask) == sk.prefix) few_put(&lds.few_count, lds.few, x.x, x.y);
+  }
+}
+
+// After the gather and a barrier: the need-th largest key among the gathered
+// items becomes sk's full threshold key (sk.need: how many items with that key
+// are still needed; sk.count: how many there are).  If they tie (count >
+// need), the same ranking on ~id among them fills ik the way the id passes
+// would, and the function returns true.
+template <int BLOCK>
+__device__ __forceinline__ bool few_rank(SelectLds<BLOCK>& lds, Radix& sk, Radix& ik, int lane) {
+  const int c = static_cast<int>(sk.count);  // <= kFew
+  const uint2 x = lane < c ? lds.few[lane] : make_uint2(0u, 0u);
+  uint32_t kg = 0u, ke = 0u;
+  for (int j = 0; j < c; ++j) {
+    const uint32_t kj = lane_of(x.x, j);
+    kg += kj > x.x ? 1u : 0u;
+    ke += kj == x.x ? 1u : 0u;
+  }
+  // the lane holding the need-th largest key (the clamp keeps L in range)
+  const int L = first_lane(__ballot(lane < c && kg < sk.need && sk.need <= kg + ke) | (1ull << (kFew - 1)));
+  sk.prefix = lane_of(x.x, L);
+  sk.mask = ~0u;
+  sk.need -= lane_of(kg, L);
+  sk.count = lane_of(ke, L);
+  if (sk.count <= sk.need) return false;  // every item with the threshold key is taken
+  const bool tied = lane < c && x.x == sk.prefix;
+  uint32_t ug = 0u, ue = 0u;
+  for (int j = 0; j < c; ++j) {
+    const bool tj = lane_of(x.x, j) == sk.prefix;
+    const uint32_t uj = lane_of(x.y, j);
+    ug += (tj && uj > x.y) ? 1u : 0u;
+    ue += (tj && uj == x.y) ? 1u : 0u;
+  }
+  const int L2 = first_lane(__ballot(tied && ug < sk.need && sk.need <= ug + ue) | (1ull << (kFew - 1)));
+  ik.prefix = lane_of(x.y, L2);
+  ik.mask = ~0u;
+  ik.need = sk.need - lane_of(ug, L2);
+  ik.count = lane_of(ue, L2);
+  return true;
 }
 
 // OR and AND of the list's keys and complemented ids over the whole
@@ -625,6 +686,7 @@ __global__ __launch_bounds__(BLOCK) void stable_topk_kernel(Source src, Sink sin
   // stays after the barrier so that pass 0 starts on the first chunk while
   // later chunks are still arriving
   clear_words<BLOCK>(&lds.hist[0][0], 3 * kBins + 3 * kSmallBins, t);
+  if (t == 0) lds.few_count = 0u;
   lds_barrier();
   __builtin_amdgcn_sched_barrier(0);
   src.template finish<VEC, NV>(aux, bits, idv);
@@ -676,19 +738,19 @@ __global__ __launch_bounds__(BLOCK) void stable_topk_kernel(Source src, Sink sin
   Radix ik{0u, 0u, 0u, 0u};
   if (m != sk.need && m <= kListCap) {
     // 3. the threshold bin as a list: each of its items writes itself at its
-    // rank and, in the same step, counts its next 8 key bits (list pass 0)
+    // pass-0 rank (every other item writes to its lane's dump slot, so the
+    // loop has no per-item branch); then list pass 0 counts the next 8 key
+    // bits
     const uint32_t d0 = sk.prefix >> 21;
 #pragma unroll
     for (int i = 0; i < N; ++i) {
-      if (((valid >> i) & 1u) && (key[i] >> 21) == d0) {
-        lds.list[rank_in_bin[i]] = make_uint2(key[i], idv[i]);
-        lds_add(lds.small[0] + ((key[i] >> 13) & 0xFFu));
-      }
+      const bool in_bin = ((valid >> i) & 1u) && (key[i] >> 21) == d0;
+      lds.list[in_bin ? rank_in_bin[i] : static_cast<uint32_t>(kListCap + lane)] = make_uint2(key[i], idv[i]);
     }
     lds_barrier();
-    advance(sk, find_digit_small<kSmallBins>(lds.small[0], sk.need, lane), 13, 0xFFu);
+    list_pass<BLOCK, 13, 8, false>(lds, 0, m, 0u, sk, t, lane);
     int q = 1;
-    bool same_ids_known = false;
+    bool same_ids_known = false, resolved = false;
     uint32_t uor = 0u, uand = 0u;
     if (sk.count == m && m > sk.need) {
       // everything fell into one bin again: look for bits shared by the whole
@@ -701,34 +763,48 @@ __global__ __launch_bounds__(BLOCK) void stable_topk_kernel(Source src, Sink sin
         sk.mask = ~0u;
       }
     }
+    // 4. the rest of the key threshold: a sub-bin of a handful of items (the
+    // usual case for smooth scores) is finished by comparison, together with
+    // its id threshold if it ties; larger ones take list passes
     do {
       if (sk.count == sk.need || sk.mask == ~0u) break;
-      list_pass<BLOCK, 5, 8, false>(lds, q++, m, 0u, sk, t, lane);
-      if (sk.count == sk.need) break;
-      list_pass<BLOCK, 0, 5, false>(lds, q++, m, 0u, sk, t, lane);
+      if (sk.count > static_cast<uint32_t>(kFew)) {
+        list_pass<BLOCK, 5, 8, false>(lds, q++, m, 0u, sk, t, lane);
+        if (sk.count == sk.need) break;
+      }
+      if (sk.count > static_cast<uint32_t>(kFew)) {
+        list_pass<BLOCK, 0, 5, false>(lds, q++, m, 0u, sk, t, lane);
+        break;
+      }
+      few_gather_list(lds, m, sk, t);
+      lds_barrier();
+      tie = few_rank(lds, sk, ik, lane);
+      resolved = true;
     } while (false);
-    // 4. id tie-break over the list items with the threshold key (then all
-    // score bits are fixed and sk.prefix is the full threshold key)
-    tie = sk.count > sk.need;
-    if (tie) {
-      ik.need = sk.need;
-      ik.count = sk.count;
-      // id digits shared by every list item (so by every tied item) are fixed
-      // without a pass
-      const uint32_t differ = same_ids_known ? (uor ^ uand) : ~0u;
-      if ((differ >> 24) == 0u) { ik.prefix |= uand & 0xFF000000u; ik.mask |= 0xFF000000u; }
-      if ((differ >> 24) == 0u && ((differ >> 16) & 0xFFu) == 0u) { ik.prefix |= uand & 0x00FF0000u; ik.mask |= 0x00FF0000u; }
-      do {
-        if (!(ik.mask & 0xFF000000u)) list_pass<BLOCK, 24, 8, true>(lds, q++, m, sk.prefix, ik, t, lane);
-        if (ik.count == ik.need) break;
-        if (!(ik.mask & 0x00FF0000u)) list_pass<BLOCK, 16, 8, true>(lds, q++, m, sk.prefix, ik, t, lane);
-        if (ik.count == ik.need) break;
-        list_pass<BLOCK, 8, 8, true>(lds, q++, m, sk.prefix, ik, t, lane);
-        if (ik.count == ik.need) break;
-        list_pass<BLOCK, 0, 8, true>(lds, q++, m, sk.prefix, ik, t, lane);
-      } while (false);
-      dup = ik.count > ik.need;  // identical (key, id) pairs straddle the boundary
+    if (!resolved) {
+      // 5. id tie-break over the list items with the threshold key (all score
+      // bits are fixed now and sk.prefix is the full threshold key)
+      tie = sk.count > sk.need;
+      if (tie) {
+        ik.need = sk.need;
+        ik.count = sk.count;
+        // id digits shared by every list item (so by every tied item) are
+        // fixed without a pass
+        const uint32_t differ = same_ids_known ? (uor ^ uand) : ~0u;
+        if ((differ >> 24) == 0u) { ik.prefix |= uand & 0xFF000000u; ik.mask |= 0xFF000000u; }
+        if ((differ >> 24) == 0u && ((differ >> 16) & 0xFFu) == 0u) { ik.prefix |= uand & 0x00FF0000u; ik.mask |= 0x00FF0000u; }
+        do {
+          if (!(ik.mask & 0xFF000000u)) list_pass<BLOCK, 24, 8, true>(lds, q++, m, sk.prefix, ik, t, lane);
+          if (ik.count == ik.need) break;
+          if (!(ik.mask & 0x00FF0000u)) list_pass<BLOCK, 16, 8, true>(lds, q++, m, sk.prefix, ik, t, lane);
+          if (ik.count == ik.need) break;
+          list_pass<BLOCK, 8, 8, true>(lds, q++, m, sk.prefix, ik, t, lane);
+          if (ik.count == ik.need) break;
+          list_pass<BLOCK, 0, 8, true>(lds, q++, m, sk.prefix, ik, t, lane);
+        } while (false);
+      }
     }
+    dup = tie && ik.count > ik.need;  // identical (key, id) pairs straddle the boundary
   } else if (m != sk.need) {
     // 3'. a bin too large for the list: the remaining passes over the registers
     do {
@@ -800,9 +876,17 @@ __global__ __launch_bounds__(BLOCK) void stable_topk_kernel(Source src, Sink sin
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
-    for (uint32_t e = lane; e < out_count; e += kWave) {
-      const uint2 x = stage[e];
-      dst.store(true, out_first + e, x.x, x.y);
+    // all reads first, then all stores; slots past out_count hold stale
+    // values, and their stores are dropped (the reads stay inside the wave's
+    // kStageCap + 64 slots)
+    constexpr int kCopies = (kStageCap + kWave - 1) / kWave;
+    uint2 x[kCopies];
+#pragma unroll
+    for (int u = 0; u < kCopies; ++u) x[u] = stage[u * kWave + lane];
+#pragma unroll
+    for (int u = 0; u < kCopies; ++u) {
+      const uint32_t e = static_cast<uint32_t>(u * kWave + lane);
+      dst.store(e < out_count, out_first + e, x[u].x, x[u].y);
     }
   } else {
 #pragma unroll

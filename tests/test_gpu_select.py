@@ -222,3 +222,24 @@ def test_rows_shorter_than_the_thread_slots(rows, c, k):
     """Rows whose last waves hold no candidate at all."""
     g = W.random_gathered(rows, c, k, seed=c, dist="uniform")
     assert_select_parity(g.scores, g.ids, k, g.name, guard=1)
+
+
+@pytest.mark.parametrize("copies,same_id", [(1, False), (3, False), (7, True), (15, False), (20, False)])
+def test_ties_at_the_threshold_in_a_small_sub_bin(copies, same_id):
+    """A few copies of the K-th largest score (so the threshold's bin holds a
+    handful of items that tie on the full key), optionally sharing one id (full
+    duplicates straddling the boundary); 20 copies exceed the comparison path
+    and take the histogram passes."""
+    rng = np.random.default_rng(900 + copies)
+    rows, c, k = 8, 8192, 2048
+    s = rng.standard_normal((rows, c), dtype=np.float32)
+    ids = W.distinct_per_row(rng, rows, c, 4 * c)
+    for r in range(rows):
+        kth = np.sort(s[r])[::-1][k - 1 + (r % 3) - 1]  # around the K-th largest
+        below = np.nonzero(s[r] < kth)[0]
+        at = rng.choice(below, copies, replace=False)
+        s[r, at] = kth
+        if same_id:
+            tied = np.nonzero(s[r] == kth)[0]
+            ids[r, tied[1:]] = ids[r, tied[0]]
+    assert_select_parity(s, ids, k, f"{copies} copies of the threshold, shared id {same_id}")
