@@ -373,20 +373,17 @@ __device__ __forceinline__ void list_common_bits(SelectLds<BLOCK>& lds, int m, i
   uand = uniform(lds.common[3]);
 }
 
-// Exclusive rank of every flagged item (flag[i] is 0 or 1) among all flagged
-// items of the row in candidate-position order.  Wave w owns the contiguous
-// positions [w*64*N, (w+1)*64*N); inside it, chunk v holds 64*VEC consecutive
-// positions, lane-major.  So a rank is: flagged items of earlier waves (one
-// number per wave, exchanged through LDS: one barrier) + of earlier chunks of
+// Exclusive rank of every flagged item (flag[i] is 0 or 1) among the flagged
+// items of its own wave, in candidate-position order; returns the wave's
+// flagged count (wave-uniform).  Wave w owns the contiguous positions
+// [w*64*N, (w+1)*64*N); inside it, chunk v holds 64*VEC consecutive
+// positions, lane-major.  So a rank is: flagged items of earlier chunks of
 // this wave (scalar) + of earlier lanes in this chunk (packed DPP scan) + of
-// earlier slots of this thread.  `segment` must belong to this call alone.
-template <int BLOCK, int VEC, int N>
-__device__ __forceinline__ void position_rank(const uint32_t (&flag)[N], uint32_t* segment, uint32_t (&rank)[N],
-                                              int lane, int w, uint32_t* wave_first = nullptr,
-                                              uint32_t* wave_count = nullptr) {
+// earlier slots of this thread.
+template <int VEC, int N>
+__device__ __forceinline__ uint32_t wave_rank(const uint32_t (&flag)[N], uint32_t (&rank)[N], int lane) {
   constexpr int NV = N / VEC;       // chunks per thread
   constexpr int NW = (NV + 3) / 4;  // packed words: 4 chunk counts of 8 bits each
-  constexpr int kWaves = BLOCK / kWave;
   // per-thread count of flagged items in each chunk (<= VEC), packed; a wave's
   // running count of one chunk is <= 64*VEC <= 128, so fields never carry
   uint32_t packed[NW];
@@ -406,30 +403,42 @@ __device__ __forceinline__ void position_rank(const uint32_t (&flag)[N], uint32_
     excl[q] = incl - packed[q];
     total[q] = lane_of(incl, kWave - 1);  // this wave's count of each chunk, packed
   }
-  uint32_t chunk_base[NV];  // flagged items of this wave before chunk v (scalar)
   uint32_t wave_total = 0;
 #pragma unroll
   for (int v = 0; v < NV; ++v) {
-    chunk_base[v] = wave_total;
-    wave_total += (total[v / 4] >> (8 * (v % 4))) & 0xFFu;
-  }
-  if (lane == 0) segment[w] = wave_total;
-  lds_barrier();
-  uint32_t before = 0;
-#pragma unroll
-  for (int i = 0; i < kWaves; ++i) before += i < w ? segment[i] : 0u;
-  before = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(before)));
-  if (wave_first != nullptr) *wave_first = before;
-  if (wave_count != nullptr) *wave_count = wave_total;
-#pragma unroll
-  for (int v = 0; v < NV; ++v) {
-    uint32_t own = before + chunk_base[v] + ((excl[v / 4] >> (8 * (v % 4))) & 0xFFu);
+    uint32_t own = wave_total + ((excl[v / 4] >> (8 * (v % 4))) & 0xFFu);
 #pragma unroll
     for (int j = 0; j < VEC; ++j) {
       rank[v * VEC + j] = own;
       own += flag[v * VEC + j];
     }
+    wave_total += (total[v / 4] >> (8 * (v % 4))) & 0xFFu;
   }
+  return wave_total;
+}
+
+// Flagged items of the waves before wave w, once every wave has published its
+// count in segment[w] and passed a barrier (wave-uniform).
+template <int BLOCK>
+__device__ __forceinline__ uint32_t waves_before(const uint32_t* segment, int w) {
+  uint32_t before = 0;
+#pragma unroll
+  for (int i = 0; i < BLOCK / kWave; ++i) before += i < w ? segment[i] : 0u;
+  return uniform(before);
+}
+
+// Exclusive rank of every flagged item among all flagged items of the row in
+// candidate-position order (one barrier).  `segment` must belong to this call
+// alone.
+template <int BLOCK, int VEC, int N>
+__device__ __forceinline__ void position_rank(const uint32_t (&flag)[N], uint32_t* segment, uint32_t (&rank)[N],
+                                              int lane, int w) {
+  const uint32_t total = wave_rank<VEC, N>(flag, rank, lane);
+  if (lane == 0) segment[w] = total;
+  lds_barrier();
+  const uint32_t before = waves_before<BLOCK>(segment, w);
+#pragma unroll
+  for (int i = 0; i < N; ++i) rank[i] += before;
 }
 
 // ---------------------------------------------------------------------------
@@ -668,6 +677,10 @@ __global__ __launch_bounds__(BLOCK) void stable_topk_kernel(Source src, Sink sin
   constexpr int NV = N / VEC;
   constexpr int kChunk = VEC * kWave;  // consecutive positions per chunk and wave
   __shared__ SelectLds<BLOCK> lds;
+  // per-wave output staging: half of a wave's slots, at most 448, plus one
+  // spare slot per lane
+  constexpr int kStageCap = kWave * N / 2 < 448 ? kWave * N / 2 : 448;
+  __shared__ uint2 stage[BLOCK / kWave][kStageCap + kWave];
 
   const int t = threadIdx.x;
   const int lane = t & (kWave - 1);
@@ -855,34 +868,33 @@ __global__ __launch_bounds__(BLOCK) void stable_topk_kernel(Source src, Sink sin
   }
 
   // 5. stable compaction and store.  Wave w's selected items fill the output
-  // slots [out_first, out_first + out_count) (its positions precede all later waves'), so
-  // each wave stages its own items in LDS (the histograms and the list are
-  // dead by now: every wave is past position_rank's barrier) and writes its
-  // range with consecutive stores.  Unselected items write to this lane's own
-  // spare slot, so the staging loop has no per-item branch.
-  uint32_t rank[N], out_first, out_count;
-  position_rank<BLOCK, VEC, N>(sel, lds.segment[1], rank, lane, w, &out_first, &out_count);
-  // items a wave can stage: half of its slots, at most 512 (a wave past that
-  // stores straight from registers)
-  constexpr int kStageCap = kWave * N / 2 < 512 ? kWave * N / 2 : 512;
-  static_assert(sizeof(SelectLds<BLOCK>) >= (BLOCK / kWave) * (kStageCap + kWave) * sizeof(uint2), "staging fits");
-  if (out_count <= static_cast<uint32_t>(kStageCap)) {
-    uint2* stage = reinterpret_cast<uint2*>(&lds) + w * (kStageCap + kWave);
+  // slots [out_first, out_first + out_count) (its positions precede all later
+  // waves'), so each wave stages its own items in its own LDS area at their
+  // rank inside the wave (unselected items write to this lane's spare slot, so
+  // the loop has no per-item branch) while the waves' counts are exchanged,
+  // then writes its range with consecutive stores.  A wave with more selected
+  // items than its area stores every item at its rank from the registers.
+  uint32_t rank[N];
+  const uint32_t out_count = wave_rank<VEC, N>(sel, rank, lane);
+  if (lane == 0) lds.segment[1][w] = out_count;
+  const bool staged = out_count <= static_cast<uint32_t>(kStageCap);  // wave-uniform
+  if (staged) {
 #pragma unroll
     for (int i = 0; i < N; ++i) {
-      const uint32_t slot = sel[i] ? rank[i] - out_first : static_cast<uint32_t>(kStageCap + lane);
-      stage[slot] = make_uint2(bits[i], idv[i]);
+      const uint32_t slot = sel[i] ? rank[i] : static_cast<uint32_t>(kStageCap + lane);
+      stage[w][slot] = make_uint2(bits[i], idv[i]);
     }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+  }
+  lds_barrier();
+  const uint32_t out_first = waves_before<BLOCK>(lds.segment[1], w);
+  if (staged) {
     // all reads first, then all stores; slots past out_count hold stale
     // values, and their stores are dropped (the reads stay inside the wave's
     // kStageCap + 64 slots)
     constexpr int kCopies = (kStageCap + kWave - 1) / kWave;
     uint2 x[kCopies];
 #pragma unroll
-    for (int u = 0; u < kCopies; ++u) x[u] = stage[u * kWave + lane];
+    for (int u = 0; u < kCopies; ++u) x[u] = stage[w][u * kWave + lane];
 #pragma unroll
     for (int u = 0; u < kCopies; ++u) {
       const uint32_t e = static_cast<uint32_t>(u * kWave + lane);
@@ -890,9 +902,7 @@ __global__ __launch_bounds__(BLOCK) void stable_topk_kernel(Source src, Sink sin
     }
   } else {
 #pragma unroll
-    for (int i = 0; i < N; ++i) {
-      dst.store(sel[i] != 0u, rank[i], bits[i], idv[i]);
-    }
+    for (int i = 0; i < N; ++i) dst.store(sel[i] != 0u, out_first + rank[i], bits[i], idv[i]);
   }
 }
 
