@@ -64,6 +64,7 @@ constexpr int kBins = 2048;      // widest digit: 11 bits
 constexpr int kSmallBins = 256;  // list passes: digits of at most 8 bits
 constexpr int kListCap = 2048;   // largest threshold bucket handled as a list
 constexpr int kFew = 16;         // threshold sub-bins this small are resolved by comparison
+constexpr int kBucket = 8;       // items list pass 0 keeps per 8-bit digit (see list_pass0)
 constexpr uint32_t kBufferWord3 = 0x00020000u;  // raw buffer resource, gfx9 family
 constexpr uint32_t kDropOffset = 0x80000000u;   // beyond any num_records used here
 
@@ -299,15 +300,14 @@ __device__ __forceinline__ void few_gather_list(SelectLds<BLOCK>& lds, int m, co
   }
 }
 
-// After the gather and a barrier: the need-th largest key among the gathered
-// items becomes sk's full threshold key (sk.need: how many items with that key
+// Given the (key, ~id) pairs of the sub-bin's sk.count items in items[] (all
+// visible to this wave): the need-th largest key among them becomes sk's full threshold key (sk.need: how many items with that key
 // are still needed; sk.count: how many there are).  If they tie (count >
 // need), the same ranking on ~id among them fills ik the way the id passes
 // would, and the function returns true.
-template <int BLOCK>
-__device__ __forceinline__ bool few_rank(SelectLds<BLOCK>& lds, Radix& sk, Radix& ik, int lane) {
+__device__ __forceinline__ bool few_rank(const uint2* items, Radix& sk, Radix& ik, int lane) {
   const int c = static_cast<int>(sk.count);  // <= kFew
-  const uint2 x = lane < c ? lds.few[lane] : make_uint2(0u, 0u);
+  const uint2 x = lane < c ? items[lane] : make_uint2(0u, 0u);
   uint32_t kg = 0u, ke = 0u;
   for (int j = 0; j < c; ++j) {
     const uint32_t kj = lane_of(x.x, j);
@@ -335,6 +335,29 @@ __device__ __forceinline__ bool few_rank(SelectLds<BLOCK>& lds, Radix& sk, Radix
   ik.need = sk.need - lane_of(ug, L2);
   ik.count = lane_of(ue, L2);
   return true;
+}
+
+// List pass 0 over the 8 key bits below the first 11 (small[0]), which also
+// sorts the list coarsely: each item's atomic returns its rank inside its
+// digit, and the first kBucket items of every digit copy their (key, ~id)
+// into bucket[digit * kBucket + rank].  So when the chosen digit holds at most
+// kBucket items they are already gathered, and no further pass or barrier is
+// needed to finish by comparison.  bucket overlays the pass-0 histograms,
+// which every wave has finished reading before the list build's barrier.
+// Returns the chosen digit's bucket.
+template <int BLOCK>
+__device__ __forceinline__ const uint2* list_pass0(SelectLds<BLOCK>& lds, int m, Radix& st, int t, int lane) {
+  uint2* bucket = reinterpret_cast<uint2*>(&lds.hist[0][0]);
+  static_assert(sizeof(lds.hist) >= kSmallBins * kBucket * sizeof(uint2), "buckets fit");
+  for (int e = t; e < m; e += BLOCK) {
+    const uint2 x = lds.list[e];
+    const uint32_t d = (x.x >> 13) & 0xFFu;
+    const uint32_t r = lds_add(lds.small[0] + d);
+    if (r < static_cast<uint32_t>(kBucket)) bucket[d * kBucket + r] = make_uint2(x.x, ~x.y);
+  }
+  lds_barrier();
+  advance(st, find_digit_small<kSmallBins>(lds.small[0], st.need, lane), 13, 0xFFu);
+  return bucket + ((st.prefix >> 13) & 0xFFu) * kBucket;
 }
 
 // OR and AND of the list's keys and complemented ids over the whole
@@ -761,7 +784,7 @@ __global__ __launch_bounds__(BLOCK) void stable_topk_kernel(Source src, Sink sin
       lds.list[in_bin ? rank_in_bin[i] : static_cast<uint32_t>(kListCap + lane)] = make_uint2(key[i], idv[i]);
     }
     lds_barrier();
-    list_pass<BLOCK, 13, 8, false>(lds, 0, m, 0u, sk, t, lane);
+    const uint2* digit_items = list_pass0(lds, m, sk, t, lane);
     int q = 1;
     bool same_ids_known = false, resolved = false;
     uint32_t uor = 0u, uand = 0u;
@@ -781,6 +804,11 @@ __global__ __launch_bounds__(BLOCK) void stable_topk_kernel(Source src, Sink sin
     // its id threshold if it ties; larger ones take list passes
     do {
       if (sk.count == sk.need || sk.mask == ~0u) break;
+      if (sk.count <= static_cast<uint32_t>(kBucket)) {
+        tie = few_rank(digit_items, sk, ik, lane);
+        resolved = true;
+        break;
+      }
       if (sk.count > static_cast<uint32_t>(kFew)) {
         list_pass<BLOCK, 5, 8, false>(lds, q++, m, 0u, sk, t, lane);
         if (sk.count == sk.need) break;
@@ -791,7 +819,7 @@ __global__ __launch_bounds__(BLOCK) void stable_topk_kernel(Source src, Sink sin
       }
       few_gather_list(lds, m, sk, t);
       lds_barrier();
-      tie = few_rank(lds, sk, ik, lane);
+      tie = few_rank(lds.few, sk, ik, lane);
       resolved = true;
     } while (false);
     if (!resolved) {
