@@ -63,8 +63,7 @@ constexpr int kWave = 64;
 constexpr int kBins = 2048;      // widest digit: 11 bits
 constexpr int kSmallBins = 256;  // list passes: digits of at most 8 bits
 constexpr int kListCap = 2048;   // largest threshold bucket handled as a list
-constexpr int kFew = 16;         // threshold sub-bins this small are resolved by comparison
-constexpr int kBucket = 8;       // items list pass 0 keeps per 8-bit digit (see list_pass0)
+constexpr int kBucket = 8;       // items a list pass keeps per digit; smaller sub-bins finish by comparison
 constexpr uint32_t kBufferWord3 = 0x00020000u;  // raw buffer resource, gfx9 family
 constexpr uint32_t kDropOffset = 0x80000000u;   // beyond any num_records used here
 
@@ -228,9 +227,6 @@ struct alignas(16) SelectLds {
   uint32_t segment[2][kWaves];     // per-wave flagged counts (dup scan, select scan)
   uint32_t sink[kWave];            // per-lane target of atomics whose item does not count
   uint32_t common[8];              // OR / AND of list keys and ids, per wave pair
-  uint2 few[kFew];                 // (key, ~id) of the items of a small threshold sub-bin
-  uint32_t few_count;              // items gathered into few (zeroed at start)
-  uint32_t pad_[3];
 };
 
 // Clear `words` (a multiple of 4) words of LDS.
@@ -263,50 +259,48 @@ __device__ __forceinline__ void radix_pass(SelectLds<BLOCK>& lds, int pass, cons
 
 // List pass q over the digit at SHIFT (BITS wide): score keys of the list
 // (BY_ID false) or complemented ids of the list items whose key is `thr`.
-// Uses small[q % 3]; after its barrier clears small[(q + 2) % 3], which pass
-// q - 1 used and pass q + 2 will use.  Pass 0 (the 8 key bits below the
-// first 11) runs right after the list is built.
+// Counts into small[q % 3] and, after its barrier, clears small[(q + 2) % 3]
+// (used by pass q - 1, next used by pass q + 2).  The pass also sorts the list
+// coarsely: each counted item's atomic returns its rank inside its digit, and
+// the first kBucket items of every digit copy their (key, ~id) into
+// bucket[digit * kBucket + rank].  Returns the chosen digit's bucket, which
+// holds all of that digit's items when it has at most kBucket of them, so the
+// threshold can then be finished by comparison with no further pass or
+// barrier.  The buckets overlay the pass-0 histograms, which every wave has
+// finished reading before the list build's barrier; each pass overwrites the
+// previous pass's buckets, which are read only when no further pass follows.
 template <int BLOCK, int SHIFT, int BITS, bool BY_ID>
-__device__ __forceinline__ void list_pass(SelectLds<BLOCK>& lds, int q, int m, uint32_t thr, Radix& st, int t,
-                                          int lane) {
+__device__ __forceinline__ const uint2* list_pass(SelectLds<BLOCK>& lds, int q, int m, uint32_t thr, Radix& st,
+                                                  int t, int lane) {
   constexpr int NB = 1 << BITS;
   constexpr uint32_t kDigitMask = NB - 1;
+  static_assert(sizeof(lds.hist) >= NB * kBucket * sizeof(uint2), "buckets fit");
   uint32_t* hist = lds.small[q % 3];
+  uint2* bucket = reinterpret_cast<uint2*>(&lds.hist[0][0]);
   for (int e = t; e < m; e += BLOCK) {
     const uint2 x = lds.list[e];
     const uint32_t v = BY_ID ? ~x.y : x.x;
-    if ((!BY_ID || x.x == thr) && (v & st.mask) == st.prefix) lds_add(hist + ((v >> SHIFT) & kDigitMask));
+    if ((!BY_ID || x.x == thr) && (v & st.mask) == st.prefix) {
+      const uint32_t d = (v >> SHIFT) & kDigitMask;
+      const uint32_t r = lds_add(hist + d);
+      if (r < static_cast<uint32_t>(kBucket)) bucket[d * kBucket + r] = make_uint2(x.x, ~x.y);
+    }
   }
   lds_barrier();
   if (t < kSmallBins / 4) *reinterpret_cast<uint4*>(lds.small[(q + 2) % 3] + 4 * t) = make_uint4(0u, 0u, 0u, 0u);
   advance(st, find_digit_small<NB>(hist, st.need, lane), SHIFT, kDigitMask);
+  return bucket + ((st.prefix >> SHIFT) & kDigitMask) * kBucket;
 }
 
-// A threshold sub-bin of at most kFew items (sk.count of them match sk's
-// prefix) is finished by comparison instead of histogram passes: its items'
-// (key, ~id) pairs are gathered from the list into lds.few, and after one
-// barrier every wave ranks them directly.  Gather at most
-// once per row (lds.few_count is zeroed only at the start).
-__device__ __forceinline__ void few_put(uint32_t* count, uint2* few, uint32_t key, uint32_t id) {
-  const uint32_t slot = lds_add(count);
-  if (slot < static_cast<uint32_t>(kFew)) few[slot] = make_uint2(key, ~id);
-}
-
-template <int BLOCK>
-__device__ __forceinline__ void few_gather_list(SelectLds<BLOCK>& lds, int m, const Radix& sk, int t) {
-  for (int e = t; e < m; e += BLOCK) {
-    const uint2 x = lds.list[e];
-    if ((x.x & sk.mask) == sk.prefix) few_put(&lds.few_count, lds.few, x.x, x.y);
-  }
-}
-
-// Given the (key, ~id) pairs of the sub-bin's sk.count items in items[] (all
-// visible to this wave): the need-th largest key among them becomes sk's full threshold key (sk.need: how many items with that key
-// are still needed; sk.count: how many there are).  If they tie (count >
-// need), the same ranking on ~id among them fills ik the way the id passes
-// would, and the function returns true.
+// Finishes the key threshold by comparison.  items[0..sk.count) hold the
+// (key, ~id) pairs of the items that match sk's prefix (sk.count <= kBucket,
+// written before a barrier this wave has passed).  The need-th largest key
+// among them becomes sk's full threshold key (sk.need: how many items with
+// that key are still needed; sk.count: how many there are).  If they tie
+// (count > need), the same ranking on ~id among the tied ones fills ik the way
+// the id passes would, and the function returns true.
 __device__ __forceinline__ bool few_rank(const uint2* items, Radix& sk, Radix& ik, int lane) {
-  const int c = static_cast<int>(sk.count);  // <= kFew
+  const int c = static_cast<int>(sk.count);  // <= kBucket
   const uint2 x = lane < c ? items[lane] : make_uint2(0u, 0u);
   uint32_t kg = 0u, ke = 0u;
   for (int j = 0; j < c; ++j) {
@@ -315,7 +309,7 @@ __device__ __forceinline__ bool few_rank(const uint2* items, Radix& sk, Radix& i
     ke += kj == x.x ? 1u : 0u;
   }
   // the lane holding the need-th largest key (the clamp keeps L in range)
-  const int L = first_lane(__ballot(lane < c && kg < sk.need && sk.need <= kg + ke) | (1ull << (kFew - 1)));
+  const int L = first_lane(__ballot(lane < c && kg < sk.need && sk.need <= kg + ke) | (1ull << (kBucket - 1)));
   sk.prefix = lane_of(x.x, L);
   sk.mask = ~0u;
   sk.need -= lane_of(kg, L);
@@ -329,7 +323,7 @@ __device__ __forceinline__ bool few_rank(const uint2* items, Radix& sk, Radix& i
     ug += (tj && uj > x.y) ? 1u : 0u;
     ue += (tj && uj == x.y) ? 1u : 0u;
   }
-  const int L2 = first_lane(__ballot(tied && ug < sk.need && sk.need <= ug + ue) | (1ull << (kFew - 1)));
+  const int L2 = first_lane(__ballot(tied && ug < sk.need && sk.need <= ug + ue) | (1ull << (kBucket - 1)));
   ik.prefix = lane_of(x.y, L2);
   ik.mask = ~0u;
   ik.need = sk.need - lane_of(ug, L2);
@@ -337,27 +331,23 @@ __device__ __forceinline__ bool few_rank(const uint2* items, Radix& sk, Radix& i
   return true;
 }
 
-// List pass 0 over the 8 key bits below the first 11 (small[0]), which also
-// sorts the list coarsely: each item's atomic returns its rank inside its
-// digit, and the first kBucket items of every digit copy their (key, ~id)
-// into bucket[digit * kBucket + rank].  So when the chosen digit holds at most
-// kBucket items they are already gathered, and no further pass or barrier is
-// needed to finish by comparison.  bucket overlays the pass-0 histograms,
-// which every wave has finished reading before the list build's barrier.
-// Returns the chosen digit's bucket.
-template <int BLOCK>
-__device__ __forceinline__ const uint2* list_pass0(SelectLds<BLOCK>& lds, int m, Radix& st, int t, int lane) {
-  uint2* bucket = reinterpret_cast<uint2*>(&lds.hist[0][0]);
-  static_assert(sizeof(lds.hist) >= kSmallBins * kBucket * sizeof(uint2), "buckets fit");
-  for (int e = t; e < m; e += BLOCK) {
-    const uint2 x = lds.list[e];
-    const uint32_t d = (x.x >> 13) & 0xFFu;
-    const uint32_t r = lds_add(lds.small[0] + d);
-    if (r < static_cast<uint32_t>(kBucket)) bucket[d * kBucket + r] = make_uint2(x.x, ~x.y);
+// The same finish for the id tie-break: items[0..ik.count) hold the tied items
+// that match ik's prefix (ik.count <= kBucket); the need-th largest ~id among
+// them becomes ik's full threshold.
+__device__ __forceinline__ void few_rank_ids(const uint2* items, Radix& ik, int lane) {
+  const int c = static_cast<int>(ik.count);
+  const uint32_t u = lane < c ? items[lane].y : 0u;
+  uint32_t g = 0u, e = 0u;
+  for (int j = 0; j < c; ++j) {
+    const uint32_t uj = lane_of(u, j);
+    g += uj > u ? 1u : 0u;
+    e += uj == u ? 1u : 0u;
   }
-  lds_barrier();
-  advance(st, find_digit_small<kSmallBins>(lds.small[0], st.need, lane), 13, 0xFFu);
-  return bucket + ((st.prefix >> 13) & 0xFFu) * kBucket;
+  const int L = first_lane(__ballot(lane < c && g < ik.need && ik.need <= g + e) | (1ull << (kBucket - 1)));
+  ik.prefix = lane_of(u, L);
+  ik.mask = ~0u;
+  ik.need -= lane_of(g, L);
+  ik.count = lane_of(e, L);
 }
 
 // OR and AND of the list's keys and complemented ids over the whole
@@ -722,7 +712,6 @@ __global__ __launch_bounds__(BLOCK) void stable_topk_kernel(Source src, Sink sin
   // stays after the barrier so that pass 0 starts on the first chunk while
   // later chunks are still arriving
   clear_words<BLOCK>(&lds.hist[0][0], 3 * kBins + 3 * kSmallBins, t);
-  if (t == 0) lds.few_count = 0u;
   lds_barrier();
   __builtin_amdgcn_sched_barrier(0);
   src.template finish<VEC, NV>(aux, bits, idv);
@@ -784,7 +773,7 @@ __global__ __launch_bounds__(BLOCK) void stable_topk_kernel(Source src, Sink sin
       lds.list[in_bin ? rank_in_bin[i] : static_cast<uint32_t>(kListCap + lane)] = make_uint2(key[i], idv[i]);
     }
     lds_barrier();
-    const uint2* digit_items = list_pass0(lds, m, sk, t, lane);
+    const uint2* items = list_pass<BLOCK, 13, 8, false>(lds, 0, m, 0u, sk, t, lane);
     int q = 1;
     bool same_ids_known = false, resolved = false;
     uint32_t uor = 0u, uand = 0u;
@@ -799,28 +788,25 @@ __global__ __launch_bounds__(BLOCK) void stable_topk_kernel(Source src, Sink sin
         sk.mask = ~0u;
       }
     }
-    // 4. the rest of the key threshold: a sub-bin of a handful of items (the
-    // usual case for smooth scores) is finished by comparison, together with
-    // its id threshold if it ties; larger ones take list passes
+    // 4. the rest of the key threshold: once the chosen digit holds at most
+    // kBucket items (the usual case for smooth scores, right after list pass
+    // 0) it is finished by comparison, together with its id threshold if it
+    // ties
     do {
       if (sk.count == sk.need || sk.mask == ~0u) break;
       if (sk.count <= static_cast<uint32_t>(kBucket)) {
-        tie = few_rank(digit_items, sk, ik, lane);
+        tie = few_rank(items, sk, ik, lane);
         resolved = true;
         break;
       }
-      if (sk.count > static_cast<uint32_t>(kFew)) {
-        list_pass<BLOCK, 5, 8, false>(lds, q++, m, 0u, sk, t, lane);
-        if (sk.count == sk.need) break;
-      }
-      if (sk.count > static_cast<uint32_t>(kFew)) {
-        list_pass<BLOCK, 0, 5, false>(lds, q++, m, 0u, sk, t, lane);
+      items = list_pass<BLOCK, 5, 8, false>(lds, q++, m, 0u, sk, t, lane);
+      if (sk.count == sk.need) break;
+      if (sk.count <= static_cast<uint32_t>(kBucket)) {
+        tie = few_rank(items, sk, ik, lane);
+        resolved = true;
         break;
       }
-      few_gather_list(lds, m, sk, t);
-      lds_barrier();
-      tie = few_rank(lds.few, sk, ik, lane);
-      resolved = true;
+      list_pass<BLOCK, 0, 5, false>(lds, q++, m, 0u, sk, t, lane);
     } while (false);
     if (!resolved) {
       // 5. id tie-break over the list items with the threshold key (all score
@@ -835,12 +821,28 @@ __global__ __launch_bounds__(BLOCK) void stable_topk_kernel(Source src, Sink sin
         if ((differ >> 24) == 0u) { ik.prefix |= uand & 0xFF000000u; ik.mask |= 0xFF000000u; }
         if ((differ >> 24) == 0u && ((differ >> 16) & 0xFFu) == 0u) { ik.prefix |= uand & 0x00FF0000u; ik.mask |= 0x00FF0000u; }
         do {
-          if (!(ik.mask & 0xFF000000u)) list_pass<BLOCK, 24, 8, true>(lds, q++, m, sk.prefix, ik, t, lane);
+          if (!(ik.mask & 0xFF000000u)) {
+            items = list_pass<BLOCK, 24, 8, true>(lds, q++, m, sk.prefix, ik, t, lane);
+            if (ik.count == ik.need) break;
+            if (ik.count <= static_cast<uint32_t>(kBucket)) {
+              few_rank_ids(items, ik, lane);
+              break;
+            }
+          }
+          if (!(ik.mask & 0x00FF0000u)) {
+            items = list_pass<BLOCK, 16, 8, true>(lds, q++, m, sk.prefix, ik, t, lane);
+            if (ik.count == ik.need) break;
+            if (ik.count <= static_cast<uint32_t>(kBucket)) {
+              few_rank_ids(items, ik, lane);
+              break;
+            }
+          }
+          items = list_pass<BLOCK, 8, 8, true>(lds, q++, m, sk.prefix, ik, t, lane);
           if (ik.count == ik.need) break;
-          if (!(ik.mask & 0x00FF0000u)) list_pass<BLOCK, 16, 8, true>(lds, q++, m, sk.prefix, ik, t, lane);
-          if (ik.count == ik.need) break;
-          list_pass<BLOCK, 8, 8, true>(lds, q++, m, sk.prefix, ik, t, lane);
-          if (ik.count == ik.need) break;
+          if (ik.count <= static_cast<uint32_t>(kBucket)) {
+            few_rank_ids(items, ik, lane);
+            break;
+          }
           list_pass<BLOCK, 0, 8, true>(lds, q++, m, sk.prefix, ik, t, lane);
         } while (false);
       }
