@@ -395,10 +395,14 @@ __device__ __forceinline__ void list_common_bits(SelectLds<BLOCK>& lds, int m, i
 // earlier slots of this thread.
 template <int VEC, int N>
 __device__ __forceinline__ uint32_t wave_rank(const uint32_t (&flag)[N], uint32_t (&rank)[N], int lane) {
-  constexpr int NV = N / VEC;       // chunks per thread
-  constexpr int NW = (NV + 3) / 4;  // packed words: 4 chunk counts of 8 bits each
-  // per-thread count of flagged items in each chunk (<= VEC), packed; a wave's
-  // running count of one chunk is <= 64*VEC <= 128, so fields never carry
+  constexpr int NV = N / VEC;  // chunks per thread
+  // per-thread count of flagged items in each chunk (<= VEC), packed into
+  // fields wide enough for a wave's running count of one chunk (<= 64*VEC):
+  // 8 bits up to VEC 2, 16 bits for VEC 4, so fields never carry
+  constexpr int kFieldBits = kWave * VEC < 256 ? 8 : 16;
+  constexpr int kPerWord = 32 / kFieldBits;
+  constexpr uint32_t kFieldMask = (1u << kFieldBits) - 1u;
+  constexpr int NW = (NV + kPerWord - 1) / kPerWord;
   uint32_t packed[NW];
 #pragma unroll
   for (int q = 0; q < NW; ++q) packed[q] = 0;
@@ -407,7 +411,7 @@ __device__ __forceinline__ uint32_t wave_rank(const uint32_t (&flag)[N], uint32_
     uint32_t c = 0;
 #pragma unroll
     for (int j = 0; j < VEC; ++j) c += flag[v * VEC + j];
-    packed[v / 4] += c << (8 * (v % 4));
+    packed[v / kPerWord] += c << (kFieldBits * (v % kPerWord));
   }
   uint32_t excl[NW], total[NW];
 #pragma unroll
@@ -419,13 +423,13 @@ __device__ __forceinline__ uint32_t wave_rank(const uint32_t (&flag)[N], uint32_
   uint32_t wave_total = 0;
 #pragma unroll
   for (int v = 0; v < NV; ++v) {
-    uint32_t own = wave_total + ((excl[v / 4] >> (8 * (v % 4))) & 0xFFu);
+    uint32_t own = wave_total + ((excl[v / kPerWord] >> (kFieldBits * (v % kPerWord))) & kFieldMask);
 #pragma unroll
     for (int j = 0; j < VEC; ++j) {
       rank[v * VEC + j] = own;
       own += flag[v * VEC + j];
     }
-    wave_total += (total[v / 4] >> (8 * (v % 4))) & 0xFFu;
+    wave_total += (total[v / kPerWord] >> (kFieldBits * (v % kPerWord))) & kFieldMask;
   }
   return wave_total;
 }
@@ -558,7 +562,18 @@ struct RankSource {
 #pragma unroll
     for (int v = 0; v < NV; ++v) {
       const int64_t at = row * local_k + j0[v] + lane_off;
-      if constexpr (VEC == 2) {
+      if constexpr (VEC == 4) {
+        const uint4 s4 = *reinterpret_cast<const uint4*>(sp[v] + at);
+        const int4 i4 = *reinterpret_cast<const int4*>(ip[v] + at);
+        bits[4 * v] = s4.x;
+        bits[4 * v + 1] = s4.y;
+        bits[4 * v + 2] = s4.z;
+        bits[4 * v + 3] = s4.w;
+        idv[4 * v] = i4.x;
+        idv[4 * v + 1] = i4.y;
+        idv[4 * v + 2] = i4.z;
+        idv[4 * v + 3] = i4.w;
+      } else if constexpr (VEC == 2) {
         const uint2 s2 = *reinterpret_cast<const uint2*>(sp[v] + at);
         const int2 i2 = *reinterpret_cast<const int2*>(ip[v] + at);
         bits[2 * v] = s2.x;
@@ -613,14 +628,23 @@ struct DenseSource {
   __device__ __forceinline__ void load(int64_t row, int first, int C, uint32_t* bits, uint32_t* idv,
                                        uint32_t*) const {
     constexpr int kChunk = VEC * kWave;
+    // the range covers whole VEC-wide loads (C rounded up stays inside the
+    // row, whose width is a multiple of VEC); values past C are ignored
+    const int span = (C + VEC - 1) / VEC * VEC;
     const __amdgpu_buffer_rsrc_t src = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<float*>(scores + row * row_stride), 0, C * static_cast<int>(sizeof(float)),
+        const_cast<float*>(scores + row * row_stride), 0, span * static_cast<int>(sizeof(float)),
         static_cast<int>(kBufferWord3));
     const int voff = first * static_cast<int>(sizeof(float));
 #pragma unroll
     for (int v = 0; v < NV; ++v) {
       const int soff = v * kChunk * static_cast<int>(sizeof(float));
-      if constexpr (VEC == 2) {
+      if constexpr (VEC == 4) {
+        const int4 x = __builtin_bit_cast(int4, __builtin_amdgcn_raw_buffer_load_b128(src, voff, soff, 0));
+        bits[4 * v] = x.x;
+        bits[4 * v + 1] = x.y;
+        bits[4 * v + 2] = x.z;
+        bits[4 * v + 3] = x.w;
+      } else if constexpr (VEC == 2) {
         const int2v x = __builtin_amdgcn_raw_buffer_load_b64(src, voff, soff, 0);
         bits[2 * v] = x.x;
         bits[2 * v + 1] = x.y;
@@ -950,12 +974,11 @@ hipError_t launch(const Source& src, const Sink& sink, bool uniform_rows, int32_
 }
 
 // 256 threads up to 2048 candidates, 512 above; the smallest item count per
-// thread that covers the row.
+// thread that covers the row.  VEC 1 and 2:
 template <int VEC, class Source, class Sink>
-hipError_t launch_sized(const Source& src, const Sink& sink, bool uniform_rows, int32_t rows, int32_t num_cand,
-                        int32_t k, hipStream_t stream) {
+hipError_t launch_sized_narrow(const Source& src, const Sink& sink, bool u, int32_t rows, int32_t num_cand,
+                               int32_t k, hipStream_t stream) {
   constexpr int kSmall = 256 * VEC;  // positions covered by 256 threads with one chunk
-  const bool u = uniform_rows;
   if (num_cand <= kSmall) return launch<256, VEC, VEC>(src, sink, u, rows, num_cand, k, stream);
   if (num_cand <= 2 * kSmall) return launch<256, VEC, 2 * VEC>(src, sink, u, rows, num_cand, k, stream);
   if (num_cand <= 4 * kSmall) return launch<256, VEC, 4 * VEC>(src, sink, u, rows, num_cand, k, stream);
@@ -963,6 +986,22 @@ hipError_t launch_sized(const Source& src, const Sink& sink, bool uniform_rows, 
   if (num_cand <= 4096) return launch<512, VEC, 8>(src, sink, u, rows, num_cand, k, stream);
   if (num_cand <= 8192) return launch<512, VEC, 16>(src, sink, u, rows, num_cand, k, stream);
   return launch<512, VEC, 32>(src, sink, u, rows, num_cand, k, stream);
+}
+
+// Any VEC (VEC 4: 256 consecutive positions per wave load).
+template <int VEC, class Source, class Sink>
+hipError_t launch_sized(const Source& src, const Sink& sink, bool uniform_rows, int32_t rows, int32_t num_cand,
+                        int32_t k, hipStream_t stream) {
+  const bool u = uniform_rows;
+  if constexpr (VEC == 4) {
+    if (num_cand <= 1024) return launch<256, 4, 4>(src, sink, u, rows, num_cand, k, stream);
+    if (num_cand <= 2048) return launch<256, 4, 8>(src, sink, u, rows, num_cand, k, stream);
+    if (num_cand <= 4096) return launch<512, 4, 8>(src, sink, u, rows, num_cand, k, stream);
+    if (num_cand <= 8192) return launch<512, 4, 16>(src, sink, u, rows, num_cand, k, stream);
+    return launch<512, 4, 32>(src, sink, u, rows, num_cand, k, stream);
+  } else {
+    return launch_sized_narrow<VEC>(src, sink, u, rows, num_cand, k, stream);
+  }
 }
 
 }  // namespace
@@ -982,11 +1021,17 @@ hipError_t launch_fused(const FusedRanks& ranks, int32_t dcp, int32_t rows, int3
   if (dcp * local_k == 0)  // no candidates: every slot is padding, nothing is read
     return launch_sized<1>(GatheredSource{nullptr, 0}, sink, true, rows, 0, k, stream);
   const RankSource src{ranks, local_k, dcp * local_k, dcp - 1};
-  bool pairs = local_k % (2 * kWave) == 0;
-  for (int r = 0; r < dcp; ++r)
-    pairs = pairs && reinterpret_cast<uintptr_t>(ranks.rank[r].scores) % 8 == 0 &&
-            reinterpret_cast<uintptr_t>(ranks.rank[r].idx) % 8 == 0;
-  if (pairs) return launch_sized<2>(src, sink, true, rows, dcp * local_k, k, stream);
+  // the widest load every rank's arrays allow: VEC consecutive slots per lane
+  // need local_k to be a multiple of 64*VEC and 4*VEC-byte aligned arrays
+  auto fits = [&](int vec) {
+    bool ok = local_k % (vec * kWave) == 0;
+    for (int r = 0; r < dcp; ++r)
+      ok = ok && reinterpret_cast<uintptr_t>(ranks.rank[r].scores) % (4 * vec) == 0 &&
+           reinterpret_cast<uintptr_t>(ranks.rank[r].idx) % (4 * vec) == 0;
+    return ok;
+  };
+  if (fits(4)) return launch_sized<4>(src, sink, true, rows, dcp * local_k, k, stream);
+  if (fits(2)) return launch_sized<2>(src, sink, true, rows, dcp * local_k, k, stream);
   return launch_sized<1>(src, sink, true, rows, dcp * local_k, k, stream);
 }
 
@@ -996,8 +1041,11 @@ hipError_t launch_local(const float* scores, int64_t score_row_stride, const int
   const DenseSource src{scores, score_row_stride, lengths, num_cols};
   const SplitSink sink{out_scores, out_idx, out_row_stride};
   const bool uniform_rows = lengths == nullptr;
-  if ((num_cols % 2 == 0) && (score_row_stride % 2 == 0) && (reinterpret_cast<uintptr_t>(scores) % 8 == 0))
-    return launch_sized<2>(src, sink, uniform_rows, rows, num_cols, k, stream);
+  auto fits = [&](int vec) {
+    return num_cols % vec == 0 && score_row_stride % vec == 0 && reinterpret_cast<uintptr_t>(scores) % (4 * vec) == 0;
+  };
+  if (fits(4)) return launch_sized<4>(src, sink, uniform_rows, rows, num_cols, k, stream);
+  if (fits(2)) return launch_sized<2>(src, sink, uniform_rows, rows, num_cols, k, stream);
   return launch_sized<1>(src, sink, uniform_rows, rows, num_cols, k, stream);
 }
 

@@ -21,16 +21,17 @@ def _gpu():
     B.load_library()
 
 
-def _dev_shards(sh, misalign=False):
-    """Device copies of the shards; ``misalign`` starts every score and index
-    array 4 bytes past an 8-byte boundary (the 4-byte load path)."""
+def _dev_shards(sh, misalign=0):
+    """Device copies of the shards; ``misalign`` = 1 starts every score and
+    index array 4 bytes past an 8-byte boundary (the 4-byte load path), 2
+    starts them 8 bytes past a 16-byte boundary (the 8-byte load path)."""
     def put(a):
         if not misalign:
             return to_dev(a)
-        flat = torch.zeros(a.size + 1, dtype=torch.from_numpy(a).dtype, device=DEV)
-        flat[1:] = to_dev(a.reshape(-1))
-        t = flat[1:].view(a.shape)
-        assert t.data_ptr() % 8 == 4
+        flat = torch.zeros(a.size + misalign, dtype=torch.from_numpy(a).dtype, device=DEV)
+        flat[misalign:] = to_dev(a.reshape(-1))
+        t = flat[misalign:].view(a.shape)
+        assert t.data_ptr() % 16 == 4 * misalign
         return t
 
     return ([put(sh.scores[r]) for r in range(sh.dcp)], [put(sh.local_idx[r]) for r in range(sh.dcp)],
@@ -53,7 +54,7 @@ def _random_shards(rows, dcp, local_k, seed, invalid_frac=0.0, span=4096, dist="
     return W.LocalShards("random", np.ascontiguousarray(scores), idx, starts, offs, k=0)
 
 
-def _fused(sh, k, guard=2, misalign=False):
+def _fused(sh, k, guard=2, misalign=0):
     """Fused merge on the GPU with canary rows around the output; returns the
     output as numpy (rows, k, 2)."""
     sc, ix, rs, offs = _dev_shards(sh, misalign)
@@ -121,12 +122,13 @@ def test_fused_ragged(rows, dcp, local_k, k, dist):
     _parity(sh, k, f"ragged rows={rows} dcp={dcp} local_k={local_k} k={k} {dist}")
 
 
-@pytest.mark.parametrize("local_k", [128, 192, 2048])
-def test_fused_4_byte_aligned_inputs(local_k):
+@pytest.mark.parametrize("local_k,shift", [(128, 1), (192, 1), (2048, 1), (2048, 2), (256, 2), (128, 2)])
+def test_fused_narrow_load_paths(local_k, shift):
     """Score and index arrays 4 bytes past an 8-byte boundary take the 4-byte
-    load path."""
-    sh = _random_shards(9, 4, local_k, seed=local_k, invalid_frac=0.05)
-    _parity(sh, 200, f"misaligned local_k={local_k}", misalign=True)
+    load path, 8 bytes past a 16-byte boundary the 8-byte one (16-byte loads
+    need 16-byte alignment and local_k a multiple of 256)."""
+    sh = _random_shards(9, 4, local_k, seed=local_k + shift, invalid_frac=0.05)
+    _parity(sh, 200, f"misaligned by {4 * shift} B, local_k={local_k}", misalign=shift)
 
 
 def test_fused_empty_shard_and_no_candidates():

@@ -91,10 +91,12 @@ def test_local_ragged(rows, cols, k):
     _parity(d.scores, k, label=f"ragged {rows}x{cols} k={k}")
 
 
-@pytest.mark.parametrize("in_pad,in_shift,out_pad", [(6, 0, 0), (5, 1, 3), (0, 1, 0), (2, 0, 9)])
+@pytest.mark.parametrize("in_pad,in_shift,out_pad", [(6, 0, 0), (5, 1, 3), (0, 1, 0), (2, 0, 9), (0, 2, 0), (4, 0, 1)])
 def test_local_strides_and_alignment(in_pad, in_shift, out_pad):
-    """Row strides wider than the rows, and inputs 4 bytes off an 8-byte
-    boundary or with an odd stride (the 4-byte load path)."""
+    """Row strides wider than the rows, and inputs off a 16-byte boundary:
+    4-byte loads for an odd stride or a 4-byte offset, 8-byte loads for an
+    even stride that is not a multiple of 4 or an 8-byte offset, 16-byte
+    loads otherwise."""
     d = W.local(rows=12, num_cols=1000, k=300, dist="levels")
     _parity(d.scores, d.k, label=f"strides {in_pad}/{in_shift}/{out_pad}", in_pad=in_pad, in_shift=in_shift,
             out_pad=out_pad)
