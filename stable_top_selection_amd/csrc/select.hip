@@ -17,7 +17,7 @@
 // positions [w*64*N, (w+1)*64*N), its lane l the positions w*64*N +
 // v*64*VEC + VEC*l + j (chunk v < N/VEC, j < VEC), so the row is read from
 // memory once, each load instruction of a wave covering 64*VEC consecutive
-// candidates (16-byte loads when VEC = 2).
+// candidates (16-byte loads of candidate pairs, or of 4 scores or indices).
 //
 // Where the candidates come from and where the result goes are template
 // policies, so one selection core serves three entry points: a gathered
@@ -36,18 +36,23 @@
 //      themselves into an LDS list at their rank.  The remaining 21 key bits
 //      are radix-selected over the list only (digits of 8, 8, 5 bits, small
 //      histograms), stopping as soon as the chosen bin holds exactly the items
-//      still needed.  A bin too large for the list falls back to the same
-//      passes over the register-resident row (digits of 11 and 10 bits).
+//      still needed.  Each list pass also keeps the first 8 items of every
+//      digit in a per-digit bucket, so once the chosen digit holds at most 8
+//      items (usually right after the first list pass) the threshold is
+//      finished by comparing those items directly.  A bin too large for the
+//      list falls back to the same passes over the register-resident row
+//      (digits of 11 and 10 bits).
 //   4. Only if more items share the threshold key than are still needed: the
 //      same radix selection on u = ~id over the tied items (largest u = lowest
-//      id).  If identical (key, id) pairs still straddle the boundary, the
-//      lowest positions win.
-//   5. Stable compaction: per-chunk selected counts packed 4 to a word, scanned
-//      across the wave with DPP and across waves through LDS (one barrier) in
-//      (wave, chunk, lane) order = candidate-position order.  A wave's selected
-//      items fill one contiguous output range; a wave stages them in LDS at
-//      their rank and writes the range with consecutive stores.  (A wave with
-//      more selected items than its staging area stores every item at its rank
+//      id), with the same finish by comparison.  If identical (key, id) pairs
+//      still straddle the boundary, the lowest positions win.
+//   5. Stable compaction: per-chunk selected counts packed into 8- or 16-bit
+//      fields, scanned across the wave with DPP, in (wave, chunk, lane) order =
+//      candidate-position order.  A wave's selected items fill one contiguous
+//      output range, so each wave stages them in its own LDS area at their rank
+//      inside the wave while the waves' counts are exchanged (one barrier),
+//      then writes its range with consecutive stores.  (A wave with more
+//      selected items than its staging area stores every item at its rank
 //      straight from registers; unselected items store to an offset past the
 //      buffer's range, which the hardware drops, so no loop has a per-item
 //      branch.)
