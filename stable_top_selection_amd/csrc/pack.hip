@@ -25,13 +25,15 @@ constexpr int kPerThread = 4;
 constexpr uint32_t kPadBits = 0xFF800000u;  // -inf
 constexpr uint32_t kPadId = 0x7FFFFFFFu;    // INT32_MAX
 
+typedef int int4v __attribute__((ext_vector_type(4)));
+
 struct PackArgs {
   PackRank rank[kMaxPackRanks];
 };
 
-__device__ __forceinline__ uint2 pack_one(uint32_t score_bits, int32_t idx, int32_t base) {
+__device__ __forceinline__ uint2 pack_one(uint32_t score_bits, int32_t idx, uint32_t base) {
   if (idx < 0) return make_uint2(kPadBits, kPadId);
-  return make_uint2(score_bits, static_cast<uint32_t>(idx) + static_cast<uint32_t>(base));
+  return make_uint2(score_bits, static_cast<uint32_t>(idx) + base);
 }
 
 template <bool VEC>
@@ -42,14 +44,18 @@ __global__ __launch_bounds__(kPackBlock) void pack_kernel(PackArgs args, int64_t
   const int j0 = (blockIdx.y * kPackBlock + threadIdx.x) * kPerThread;
   if (j0 >= local_k) return;
   const PackRank& pr = args.rank[r];
-  const int32_t base = pr.row_starts[row] + pr.rank_offset;  // wraps like the id sum
+  // two's-complement wrap, like the id sum
+  const uint32_t base = static_cast<uint32_t>(pr.row_starts[row]) + static_cast<uint32_t>(pr.rank_offset);
   const int64_t src = row * src_row_stride + j0;
   uint2* out = reinterpret_cast<uint2*>(dst + row * dst_row_stride + static_cast<int64_t>(r) * local_k + j0);
   if (VEC && j0 + kPerThread <= local_k) {
-    const uint4 s = *reinterpret_cast<const uint4*>(pr.scores + src);
-    const int4 i = *reinterpret_cast<const int4*>(pr.idx + src);
-    const uint2 c0 = pack_one(s.x, i.x, base), c1 = pack_one(s.y, i.y, base);
-    const uint2 c2 = pack_one(s.z, i.z, base), c3 = pack_one(s.w, i.w, base);
+    // the local arrays are read once: non-temporal loads; the packed buffer is
+    // read again by the select right after, so its stores keep the default
+    // policy
+    const int4v s = __builtin_nontemporal_load(reinterpret_cast<const int4v*>(pr.scores + src));
+    const int4v i = __builtin_nontemporal_load(reinterpret_cast<const int4v*>(pr.idx + src));
+    const uint2 c0 = pack_one(static_cast<uint32_t>(s.x), i.x, base), c1 = pack_one(static_cast<uint32_t>(s.y), i.y, base);
+    const uint2 c2 = pack_one(static_cast<uint32_t>(s.z), i.z, base), c3 = pack_one(static_cast<uint32_t>(s.w), i.w, base);
     reinterpret_cast<uint4*>(out)[0] = make_uint4(c0.x, c0.y, c1.x, c1.y);
     reinterpret_cast<uint4*>(out)[1] = make_uint4(c2.x, c2.y, c3.x, c3.y);
   } else {
