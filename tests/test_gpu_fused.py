@@ -195,3 +195,24 @@ def test_fused_unsupported_and_invalid():
     with pytest.raises(B.DcpTopkError) as e:  # output overlaps rank 0's scores
         B.merge_fused(sc, ix, rs, offs, 32, out=alias)
     assert e.value.status == B.EINVAL
+
+
+def test_fused_row_offsets_beyond_2_gib():
+    """40960 rows (each rank's arrays 320 MiB, the output 640 MiB): element
+    offsets past 2^31 bytes in the per-rank arrays and the output.  The rows
+    repeat a seeded 64-row block; repeats are checked against the oracle."""
+    sh = W.prefill(rows=64, seed=405)
+    reps = 640
+    sc = [to_dev(sh.scores[r]).repeat(reps, 1) for r in range(sh.dcp)]
+    ix = [to_dev(sh.local_idx[r]).repeat(reps, 1) for r in range(sh.dcp)]
+    rs = [to_dev(sh.row_starts[r]).repeat(reps) for r in range(sh.dcp)]
+    out = B.merge_fused(sc, ix, rs, [int(x) for x in sh.rank_offsets], sh.k)
+    torch.cuda.synchronize()
+    assert out.numel() * 4 > 2**31 // 4
+    want_s, want_i = O.merge(sh.scores, sh.local_idx, sh.row_starts, sh.rank_offsets, sh.k)
+    o = out.view(reps, 64, sh.k, 2)
+    for r in (0, reps // 3, reps - 1):
+        got = o[r].cpu().numpy()
+        assert np.array_equal(got[..., 0].view(np.uint32), want_s.view(np.uint32)) and np.array_equal(got[..., 1], want_i)
+    del sc, ix, rs, out
+    torch.cuda.empty_cache()

@@ -9,6 +9,7 @@ import pytest
 import torch
 
 from gpu_helpers import DEV, assert_select_parity, gpu_select, to_dev
+from oracle import stable_topk as O
 from stable_top_selection_amd import binding as B
 from stable_top_selection_amd import workloads as W
 
@@ -243,3 +244,23 @@ def test_ties_at_the_threshold_in_a_small_sub_bin(copies, same_id):
             tied = np.nonzero(s[r] == kth)[0]
             ids[r, tied[1:]] = ids[r, tied[0]]
     assert_select_parity(s, ids, k, f"{copies} copies of the threshold, shared id {same_id}")
+
+
+def test_row_offsets_beyond_2_gib():
+    """40960 rows of 8192 candidates (2.5 GiB of input, 640 MiB of output):
+    row offsets past 2^31 bytes.  The rows repeat a seeded 64-row block, so
+    every output row is checked against the oracle's result for its block row."""
+    g = W.decode(64, seed=404)
+    reps = 640
+    block = to_dev(g.interleaved())
+    cand = block.repeat(reps, 1, 1)
+    assert cand.numel() * 4 > 2**31
+    out = B.select(cand, g.k)
+    torch.cuda.synchronize()
+    want_s, want_i = O.select(g.scores, g.ids, g.k)
+    want = np.stack([want_s.view(np.int32), want_i], axis=-1)
+    o = out.view(reps, 64, g.k, 2)
+    for r in (0, 1, reps // 2, reps - 1):
+        assert np.array_equal(o[r].cpu().numpy(), want), f"block repeat {r} differs"
+    del cand, out
+    torch.cuda.empty_cache()
