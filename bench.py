@@ -177,8 +177,11 @@ def bench_select(run, g, steps, warmup, trials, cold=True):
     us = [1e3 * m / launches for m in ms]
     del graph, tensors
     run.torch.cuda.empty_cache()
-    return {"us_per_launch": statistics.median(us), "us_trials": [round(x, 4) for x in us], "launches": launches,
-            "pool_buffers": n, "outputs_checked": checked}
+    med = statistics.median(us)
+    gbps = select_bytes(rows, c, k) / (med * 1e-6) / 1e9
+    return {"us_per_launch": med, "us_trials": [round(x, 4) for x in us], "launches": launches,
+            "pool_buffers": n, "outputs_checked": checked, "candidates_per_s": rows * c / (med * 1e-6),
+            "GBps": round(gbps, 1), "frac_of_peak": round(gbps / PEAK_HBM_GBS, 4)}
 
 
 def bench_eager(run, g, steps, trials):
@@ -252,13 +255,21 @@ def bench_prefill(run, trials):
     ms_sel = run.time_graph(g2, trials)
     merge_ms = statistics.median(ms)
     sel_ms = statistics.median(ms_sel)
-    sel_bytes = 8 * select_bytes(1024, dcp * lk, k)
-    pack_bytes = 8 * dcp * 1024 * lk * (4 + 4 + 8) + dcp * T * 4
+    chunks = -(-T // 1024)
+    sel_bytes = chunks * select_bytes(1024, dcp * lk, k)
+    pack_bytes = chunks * dcp * 1024 * lk * (4 + 4 + 8) + dcp * T * 4
+    pack_ms = merge_ms - sel_ms
+    gb = lambda b, t_ms: b / (t_ms * 1e-3) / 1e9  # noqa: E731
     return {"workload": f"prefill chunked: T={T}, DCP {dcp} x local K {lk}, K {k}, 1024-row chunks",
             "merge_ms": round(merge_ms, 4), "merge_trials_ms": [round(x, 4) for x in ms],
-            "select_only_ms": round(sel_ms, 4), "pack_ms_by_difference": round(merge_ms - sel_ms, 4),
-            "merge_GBps": round((sel_bytes + pack_bytes) / (merge_ms * 1e-3) / 1e9, 1),
-            "select_GBps_L2_warm_workspace": round(sel_bytes / (sel_ms * 1e-3) / 1e9, 1),
+            "select_only_ms": round(sel_ms, 4), "pack_ms_by_difference": round(pack_ms, 4),
+            "per_chunk_select_us": round(1e3 * sel_ms / chunks, 2), "per_chunk_pack_us": round(1e3 * pack_ms / chunks, 2),
+            "merge_GBps": round(gb(sel_bytes + pack_bytes, merge_ms), 1),
+            "select_GBps_L2_warm_workspace": round(gb(sel_bytes, sel_ms), 1),
+            "select_frac_of_peak": round(gb(sel_bytes, sel_ms) / PEAK_HBM_GBS, 4),
+            "pack_GBps": round(gb(pack_bytes, pack_ms), 1),
+            "pack_frac_of_peak": round(gb(pack_bytes, pack_ms) / PEAK_HBM_GBS, 4),
+            "merge_candidates_per_s": round(T * dcp * lk / (merge_ms * 1e-3)),
             "rows_checked": int(len(rows))}
 
 
@@ -494,7 +505,9 @@ def main():
             gd = W.decode(rows)
             cold = bench_select(run, gd, args.steps, args.warmup, args.trials, cold=True)
             hot = bench_select(run, gd, args.steps, args.warmup, args.trials, cold=False)
-            sweep[f"rows{rows}"] = {"cold_us": round(cold["us_per_launch"], 3), "warm_us": round(hot["us_per_launch"], 3)}
+            sweep[f"rows{rows}"] = {"cold_us": round(cold["us_per_launch"], 3), "warm_us": round(hot["us_per_launch"], 3),
+                                    "cold_candidates_per_s": round(cold["candidates_per_s"]), "cold_GBps": cold["GBps"],
+                                    "cold_frac_of_peak": cold["frac_of_peak"]}
             log(f"[decode rows={rows}] cold {cold['us_per_launch']:.3f} us, warm {hot['us_per_launch']:.3f} us")
         extra["decode_latency_us"] = sweep
     if "tie_heavy" in configs:
@@ -502,7 +515,9 @@ def main():
         cold = bench_select(run, gt, args.steps, args.warmup, args.trials, cold=True)
         hot = bench_select(run, gt, args.steps, args.warmup, args.trials, cold=False)
         extra["tie_heavy_latency_us"] = {"rows": gt.rows, "cold_us": round(cold["us_per_launch"], 3),
-                                         "warm_us": round(hot["us_per_launch"], 3)}
+                                         "warm_us": round(hot["us_per_launch"], 3),
+                                         "cold_candidates_per_s": round(cold["candidates_per_s"]),
+                                         "cold_GBps": cold["GBps"], "cold_frac_of_peak": cold["frac_of_peak"]}
         log(f"[tie_heavy] cold {cold['us_per_launch']:.3f} us, warm {hot['us_per_launch']:.3f} us")
     if "prefill" in configs:
         extra["prefill"] = bench_prefill(run, args.trials)
