@@ -242,7 +242,7 @@ struct alignas(16) SelectLds {
                                    // one write-only dump slot per lane
   uint32_t segment[2][kWaves];     // per-wave flagged counts (dup scan, select scan)
   uint32_t sink[kWave];            // per-lane target of atomics whose item does not count
-  uint32_t common[8];              // OR / AND of list keys and ids, per wave pair
+  uint32_t common[4];              // OR / AND of the list's keys and of its complemented ids
 };
 
 // Clear `words` (a multiple of 4) words of LDS.
@@ -366,10 +366,31 @@ __device__ __forceinline__ void few_rank_ids(const uint2* items, Radix& ik, int 
   ik.count = lane_of(e, L);
 }
 
+// OR / AND of v over the wave (wave-uniform): DPP row shifts inside each row
+// of 16 lanes (lanes shifted in from outside the row keep the identity), then
+// the four row results from lanes 15, 31, 47 and 63.
+__device__ __forceinline__ uint32_t wave_or(uint32_t v) {
+  v |= static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x111, 0xf, 0xf, false));
+  v |= static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x112, 0xf, 0xf, false));
+  v |= static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x114, 0xf, 0xf, false));
+  v |= static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x118, 0xf, 0xf, false));
+  return lane_of(v, 15) | lane_of(v, 31) | lane_of(v, 47) | lane_of(v, 63);
+}
+
+__device__ __forceinline__ uint32_t wave_and(uint32_t v) {
+  v &= static_cast<uint32_t>(__builtin_amdgcn_update_dpp(-1, static_cast<int>(v), 0x111, 0xf, 0xf, false));
+  v &= static_cast<uint32_t>(__builtin_amdgcn_update_dpp(-1, static_cast<int>(v), 0x112, 0xf, 0xf, false));
+  v &= static_cast<uint32_t>(__builtin_amdgcn_update_dpp(-1, static_cast<int>(v), 0x114, 0xf, 0xf, false));
+  v &= static_cast<uint32_t>(__builtin_amdgcn_update_dpp(-1, static_cast<int>(v), 0x118, 0xf, 0xf, false));
+  return lane_of(v, 15) & lane_of(v, 31) & lane_of(v, 47) & lane_of(v, 63);
+}
+
 // OR and AND of the list's keys and complemented ids over the whole
-// workgroup (bits where every list item agrees: ~(or ^ and)).  One barrier.
+// workgroup (bits where every list item agrees: ~(or ^ and)): DPP reductions
+// inside each wave, then LDS atomics into lds.common[0..3], which the kernel
+// initialised before its first barrier.  One barrier; call at most once.
 template <int BLOCK>
-__device__ __forceinline__ void list_common_bits(SelectLds<BLOCK>& lds, int m, int t, int lane, int w, uint32_t& kor,
+__device__ __forceinline__ void list_common_bits(SelectLds<BLOCK>& lds, int m, int t, int lane, uint32_t& kor,
                                                  uint32_t& kand, uint32_t& uor, uint32_t& uand) {
   uint32_t a = 0u, b = ~0u, c = 0u, d = ~0u;
   for (int e = t; e < m; e += BLOCK) {
@@ -379,16 +400,10 @@ __device__ __forceinline__ void list_common_bits(SelectLds<BLOCK>& lds, int m, i
     c |= ~x.y;
     d &= ~x.y;
   }
-  // fold across the wave, then across waves through LDS atomics
-#pragma unroll
-  for (int s = 1; s < kWave; s <<= 1) {
-    a |= __shfl_xor(a, s);
-    b &= __shfl_xor(b, s);
-    c |= __shfl_xor(c, s);
-    d &= __shfl_xor(d, s);
-  }
-  if (w == 0 && lane < 8) lds.common[lane] = (lane & 1) ? ~0u : 0u;  // or-slots 0, and-slots ~0
-  lds_barrier();
+  a = wave_or(a);
+  b = wave_and(b);
+  c = wave_or(c);
+  d = wave_and(d);
   if (lane == 0) {
     __hip_atomic_fetch_or(lds.common + 0, a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     __hip_atomic_fetch_and(lds.common + 1, b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
@@ -752,6 +767,7 @@ __global__ __launch_bounds__(BLOCK) void stable_topk_kernel(Source src, Sink sin
   // stays after the barrier so that pass 0 starts on the first chunk while
   // later chunks are still arriving
   clear_words<BLOCK>(&lds.hist[0][0], 3 * kBins + 3 * kSmallBins, t);
+  if (t < 4) lds.common[t] = (t & 1) ? ~0u : 0u;  // OR slots 0, AND slots ~0 (list_common_bits)
   lds_barrier();
   __builtin_amdgcn_sched_barrier(0);
   src.template finish<VEC, NV>(aux, bits, idv);
@@ -821,7 +837,7 @@ __global__ __launch_bounds__(BLOCK) void stable_topk_kernel(Source src, Sink sin
       // everything fell into one bin again: look for bits shared by the whole
       // list (identical scores, as on tie-heavy rows) and skip their passes
       uint32_t kor, kand;
-      list_common_bits(lds, m, t, lane, w, kor, kand, uor, uand);
+      list_common_bits(lds, m, t, lane, kor, kand, uor, uand);
       same_ids_known = true;
       if (kor == kand) {  // every list item has the same key
         sk.prefix = kor;
@@ -928,11 +944,19 @@ __global__ __launch_bounds__(BLOCK) void stable_topk_kernel(Source src, Sink sin
     // them, so (key & mask) >= prefix is simply key >= prefix
 #pragma unroll
     for (int i = 0; i < N; ++i) sel[i] = (key[i] >= sk.prefix) & ((valid >> i) & 1u);
+  } else if (!dup) {
+    // the tied items (key == threshold) are taken by complemented id; the id
+    // passes leave ik.prefix zero below ik.mask, so u >= prefix is the test
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const uint32_t u = ~idv[i];
+      sel[i] = (key[i] > sk.prefix || (key[i] == sk.prefix && u >= ik.prefix)) & ((valid >> i) & 1u);
+    }
   } else {
 #pragma unroll
     for (int i = 0; i < N; ++i) {
       const uint32_t u = ~idv[i];
-      const bool wins = u >= ik.prefix && (u != ik.prefix || !dup || duprank[i] < ik.need);
+      const bool wins = u > ik.prefix || (u == ik.prefix && duprank[i] < ik.need);
       sel[i] = (key[i] > sk.prefix || (key[i] == sk.prefix && wins)) & ((valid >> i) & 1u);
     }
   }
