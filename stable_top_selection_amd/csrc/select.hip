@@ -308,6 +308,30 @@ __device__ __forceinline__ const uint2* list_pass(SelectLds<BLOCK>& lds, int q, 
   return bucket + ((st.prefix >> SHIFT) & kDigitMask) * kBucket;
 }
 
+// The id tie-break's list pass: like list_pass with BY_ID, but over the
+// digit of `bits` (<= 8) bits at a run-time `shift`, so that the digits can
+// start at the highest bit where the tied items' ids differ.
+template <int BLOCK>
+__device__ __forceinline__ const uint2* list_pass_ids(SelectLds<BLOCK>& lds, int q, int m, uint32_t thr, Radix& st,
+                                                      int shift, int bits, int t, int lane) {
+  const uint32_t dmask = (1u << bits) - 1u;
+  uint32_t* hist = lds.small[q % 3];
+  uint2* bucket = reinterpret_cast<uint2*>(&lds.hist[0][0]);
+  for (int e = t; e < m; e += BLOCK) {
+    const uint2 x = lds.list[e];
+    const uint32_t v = ~x.y;
+    if (x.x == thr && (v & st.mask) == st.prefix) {
+      const uint32_t d = (v >> shift) & dmask;
+      const uint32_t r = lds_add(hist + d);
+      if (r < static_cast<uint32_t>(kBucket)) bucket[d * kBucket + r] = make_uint2(x.x, v);
+    }
+  }
+  lds_barrier();
+  if (t < kSmallBins / 4) *reinterpret_cast<uint4*>(lds.small[(q + 2) % 3] + 4 * t) = make_uint4(0u, 0u, 0u, 0u);
+  advance(st, find_digit_small<kSmallBins>(hist, st.need, lane), shift, dmask);
+  return bucket + ((st.prefix >> shift) & dmask) * kBucket;
+}
+
 // Finishes the key threshold by comparison.  items[0..sk.count) hold the
 // (key, ~id) pairs of the items that match sk's prefix (sk.count <= kBucket,
 // written before a barrier this wave has passed).  The need-th largest key
@@ -871,36 +895,33 @@ __global__ __launch_bounds__(BLOCK) void stable_topk_kernel(Source src, Sink sin
       if (tie) {
         ik.need = sk.need;
         ik.count = sk.count;
-        // id digits shared by every list item (so by every tied item) are
-        // fixed without a pass
+        // 8-bit digits of ~id from the highest bit where the list items' ids
+        // can differ: the bits above it are shared by every list item (so by
+        // every tied item) and are fixed without a pass
         const uint32_t differ = same_ids_known ? (uor ^ uand) : ~0u;
-        if ((differ >> 24) == 0u) { ik.prefix |= uand & 0xFF000000u; ik.mask |= 0xFF000000u; }
-        if ((differ >> 24) == 0u && ((differ >> 16) & 0xFFu) == 0u) { ik.prefix |= uand & 0x00FF0000u; ik.mask |= 0x00FF0000u; }
-        do {
-          if (!(ik.mask & 0xFF000000u)) {
-            items = list_pass<BLOCK, 24, 8, true>(lds, q++, m, sk.prefix, ik, t, lane);
+        if (differ == 0u) {
+          // every list item has the same id: the tied items are full
+          // duplicates, and positions decide among them
+          ik.prefix = uand;
+          ik.mask = ~0u;
+        } else {
+          int hb = 31 - __builtin_clz(differ);
+          if (hb < 31) {
+            ik.mask = ~0u << (hb + 1);
+            ik.prefix = uand & ik.mask;
+          }
+          for (;;) {  // at most 4 passes
+            const int shift = hb >= 7 ? hb - 7 : 0;
+            items = list_pass_ids(lds, q++, m, sk.prefix, ik, shift, hb - shift + 1, t, lane);
             if (ik.count == ik.need) break;
             if (ik.count <= static_cast<uint32_t>(kBucket)) {
               few_rank_ids(items, ik, lane);
               break;
             }
+            if (shift == 0) break;
+            hb = shift - 1;
           }
-          if (!(ik.mask & 0x00FF0000u)) {
-            items = list_pass<BLOCK, 16, 8, true>(lds, q++, m, sk.prefix, ik, t, lane);
-            if (ik.count == ik.need) break;
-            if (ik.count <= static_cast<uint32_t>(kBucket)) {
-              few_rank_ids(items, ik, lane);
-              break;
-            }
-          }
-          items = list_pass<BLOCK, 8, 8, true>(lds, q++, m, sk.prefix, ik, t, lane);
-          if (ik.count == ik.need) break;
-          if (ik.count <= static_cast<uint32_t>(kBucket)) {
-            few_rank_ids(items, ik, lane);
-            break;
-          }
-          list_pass<BLOCK, 0, 8, true>(lds, q++, m, sk.prefix, ik, t, lane);
-        } while (false);
+        }
       }
     }
     dup = tie && ik.count > ik.need;  // identical (key, id) pairs straddle the boundary

@@ -264,3 +264,16 @@ def test_row_offsets_beyond_2_gib():
         assert np.array_equal(o[r].cpu().numpy(), want), f"block repeat {r} differs"
     del cand, out
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("c,k", [(1000, 300), (2048, 2047), (300, 1)])
+def test_rows_of_one_repeated_candidate(c, k):
+    """Every candidate identical (same score bits and id): the first k
+    positions are taken, through the list path's all-duplicates branch."""
+    rows = 3
+    s = np.full((rows, c), 1.5, np.float32)
+    s[1] = -np.inf
+    s[2] = -0.0
+    ids = np.full((rows, c), 77, np.int32)
+    ids[1] = 2**31 - 1
+    assert_select_parity(s, ids, k, f"one repeated candidate, C={c} k={k}")
