@@ -89,6 +89,9 @@ typedef int int4v __attribute__((ext_vector_type(4)));
 // hold.
 constexpr uint32_t kPadBits = 0xFF800000u;  // -inf
 constexpr uint32_t kPadId = 0x7FFFFFFFu;    // INT32_MAX
+constexpr uint32_t kPadKey = 0x007FFFFFu;   // the score key of -inf
+constexpr uint32_t kPadBin = kPadKey >> 21; // its pass-0 bin
+constexpr int kPadWords = 8;                // pass-0 counters of padding keys
 
 // LDS-only workgroup barrier: waits for this wave's LDS traffic, not for its
 // outstanding global loads, so the row's loads stay in flight across it.
@@ -176,6 +179,34 @@ __device__ __forceinline__ Digit find_digit(const uint32_t* hist, uint32_t need,
   return d;
 }
 
+// find_digit over the pass-0 histogram with `extra` items added to bin
+// `extra_bin` (the padding keys, which pass 0 counts apart).
+__device__ __forceinline__ Digit find_digit_pass0(const uint32_t* hist, uint32_t need, int lane, uint32_t extra_bin,
+                                                  uint32_t extra) {
+  constexpr int PER = kBins / kWave;
+  constexpr int VECS = PER / 4;
+  const uint4* p = reinterpret_cast<const uint4*>(hist + kBins - PER * (lane + 1));
+  uint32_t sum = lane == static_cast<int>((kBins - 1 - extra_bin) / PER) ? extra : 0u;
+#pragma unroll
+  for (int i = 0; i < VECS; ++i) {
+    const uint4 x = p[(i + lane) & (VECS - 1)];
+    sum += x.x + x.y + x.z + x.w;
+  }
+  const uint32_t incl = wave_inclusive_scan(sum, lane);
+  const int L = first_lane(__ballot(incl >= need) | (1ull << 63));
+  const uint32_t above_l = lane_of(incl, L) - lane_of(sum, L);
+  const int top = kBins - PER * L - 1;
+  uint32_t h = lane < PER ? hist[top - lane] : 0u;
+  h += (lane < PER && static_cast<uint32_t>(top - lane) == extra_bin) ? extra : 0u;
+  const uint32_t incl2 = wave_inclusive_scan(h, lane);
+  const int i = first_lane(__ballot(lane < PER && above_l + incl2 >= need) | (1ull << (PER - 1)));
+  Digit d;
+  d.digit = static_cast<uint32_t>(top - i);
+  d.count = lane_of(h, i);
+  d.above = above_l + lane_of(incl2, i) - d.count;
+  return d;
+}
+
 // The same search for the small histograms of the list passes (NB <= 256):
 // lane l holds PER = max(1, NB/64) bins; the bin inside lane L is resolved in
 // scalar registers.
@@ -238,6 +269,7 @@ struct alignas(16) SelectLds {
   static constexpr int kWaves = BLOCK / kWave;
   uint32_t hist[3][kBins];         // pass 0 (hist[0]) and the register passes, rotating
   uint32_t small[3][kSmallBins];   // list passes, rotating
+  uint32_t padcnt[kPadWords];      // pass 0: counts of padding keys, by lane % kPadWords
   uint2 list[kListCap + kWave];    // (key, id) of the items in the pass-0 threshold bin, then
                                    // one write-only dump slot per lane
   uint32_t segment[2][kWaves];     // per-wave flagged counts (dup scan, select scan)
@@ -790,7 +822,7 @@ __global__ __launch_bounds__(BLOCK) void stable_topk_kernel(Source src, Sink sin
   // clear the histograms while the loads are in flight; the key transform
   // stays after the barrier so that pass 0 starts on the first chunk while
   // later chunks are still arriving
-  clear_words<BLOCK>(&lds.hist[0][0], 3 * kBins + 3 * kSmallBins, t);
+  clear_words<BLOCK>(&lds.hist[0][0], 3 * kBins + 3 * kSmallBins + kPadWords, t);
   if (t < 4) lds.common[t] = (t & 1) ? ~0u : 0u;  // OR slots 0, AND slots ~0 (list_common_bits)
   lds_barrier();
   __builtin_amdgcn_sched_barrier(0);
@@ -824,19 +856,31 @@ __global__ __launch_bounds__(BLOCK) void stable_topk_kernel(Source src, Sink sin
 #pragma unroll
   for (int i = 0; i < N; ++i) key[i] = score_key(bits[i]);
 
-  // 2. pass 0: histogram of the top 11 bits; each item keeps its rank in its bin
+  // 2. pass 0: histogram of the top 11 bits; each item keeps its rank in its
+  // bin.  Padding keys (-inf: empty shard slots, which can fill whole ranks)
+  // would all hit one bin, and LDS atomics to one address serialise, so they
+  // count into kPadWords words instead (by lane) and join their bin in the
+  // digit search (and, if that bin is the threshold's, in the list).
   uint32_t rank_in_bin[N];
+  uint32_t* pad_word = lds.padcnt + (lane % kPadWords);
   if constexpr (FULL) {
 #pragma unroll
-    for (int i = 0; i < N; ++i) rank_in_bin[i] = lds_add(lds.hist[0] + (key[i] >> 21));
+    for (int i = 0; i < N; ++i) rank_in_bin[i] = lds_add(key[i] == kPadKey ? pad_word : lds.hist[0] + (key[i] >> 21));
   } else {
     uint32_t* sink = lds.sink + lane;
 #pragma unroll
-    for (int i = 0; i < N; ++i) rank_in_bin[i] = lds_add((valid >> i) & 1u ? lds.hist[0] + (key[i] >> 21) : sink);
+    for (int i = 0; i < N; ++i)
+      rank_in_bin[i] =
+          lds_add((valid >> i) & 1u ? (key[i] == kPadKey ? pad_word : lds.hist[0] + (key[i] >> 21)) : sink);
   }
   lds_barrier();
+  // padding keys counted in pass 0, in total and in the words before this lane's
+  const uint4 pw0 = *reinterpret_cast<const uint4*>(lds.padcnt);
+  const uint4 pw1 = *reinterpret_cast<const uint4*>(lds.padcnt + 4);
+  const uint32_t pad_total = pw0.x + pw0.y + pw0.z + pw0.w + pw1.x + pw1.y + pw1.z + pw1.w;
+  static_assert(kPadWords == 8, "two uint4 reads");
   Radix sk{0u, 0u, static_cast<uint32_t>(k), 0u};
-  advance(sk, find_digit<kBins>(lds.hist[0], sk.need, lane), 21, 0x7FFu);
+  advance(sk, find_digit_pass0(lds.hist[0], sk.need, lane, kPadBin, pad_total), 21, 0x7FFu);
 
   const uint32_t m = sk.count;  // items in the threshold bin
   bool tie = false, dup = false;
@@ -847,6 +891,18 @@ __global__ __launch_bounds__(BLOCK) void stable_topk_kernel(Source src, Sink sin
     // loop has no per-item branch); then list pass 0 counts the next 8 key
     // bits
     const uint32_t d0 = sk.prefix >> 21;
+    if (d0 == kPadBin) {
+      // padding keys were ranked per lane: place them after the bin's other
+      // items, lane by lane
+      const uint32_t pw[kPadWords] = {pw0.x, pw0.y, pw0.z, pw0.w, pw1.x, pw1.y, pw1.z, pw1.w};
+      uint32_t before = 0u;
+#pragma unroll
+      for (int j = 0; j < kPadWords; ++j) before += j < lane % kPadWords ? pw[j] : 0u;
+      const uint32_t pad_base = lds.hist[0][kPadBin] + before;
+#pragma unroll
+      for (int i = 0; i < N; ++i)
+        if (key[i] == kPadKey) rank_in_bin[i] += pad_base;
+    }
 #pragma unroll
     for (int i = 0; i < N; ++i) {
       const bool in_bin = ((valid >> i) & 1u) && (key[i] >> 21) == d0;
