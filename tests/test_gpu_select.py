@@ -277,3 +277,17 @@ def test_rows_of_one_repeated_candidate(c, k):
     ids = np.full((rows, c), 77, np.int32)
     ids[1] = 2**31 - 1
     assert_select_parity(s, ids, k, f"one repeated candidate, C={c} k={k}")
+
+
+@pytest.mark.parametrize("c,k,pad,misalign", [(3000, 2000, 0.5, False), (1200, 1000, 0.6, True),
+                                              (8192, 2048, 0.78, False), (5000, 4990, 0.3, False)])
+def test_padding_in_the_threshold_bin(c, k, pad, misalign):
+    """Fewer real candidates than k, so the threshold falls among the padding
+    keys, which pass 0 counts apart: padding slots plus real -inf scores with
+    their own ids (ties on the -inf key, broken by id, then by position)."""
+    g = W.random_gathered(4, c, k, seed=c + k, dist="normal", pad_frac=pad)
+    s, ids = g.scores.copy(), g.ids.copy()
+    rng = np.random.default_rng(c)
+    real_inf = rng.random(s.shape) < 0.02
+    s[real_inf] = -np.inf
+    assert_select_parity(s, ids, k, f"padding threshold C={c} k={k} pad={pad}", misalign=misalign)
