@@ -441,21 +441,15 @@ __device__ __forceinline__ uint32_t wave_and(uint32_t v) {
   return lane_of(v, 15) & lane_of(v, 31) & lane_of(v, 47) & lane_of(v, 63);
 }
 
-// OR and AND of the list's keys and complemented ids over the whole
-// workgroup (bits where every list item agrees: ~(or ^ and)): DPP reductions
-// inside each wave, then LDS atomics into lds.common[0..3], which the kernel
-// initialised before its first barrier.  One barrier; call at most once.
+// OR and AND over the whole workgroup of this thread's partial key OR / AND
+// (a, b) and complemented-id OR / AND (c, d): bits where every counted item
+// agrees are ~(or ^ and).  DPP reductions inside each wave, then LDS atomics
+// into lds.common[0..3], which the kernel initialised before its first
+// barrier.  One barrier; a kernel calls it at most once.
 template <int BLOCK>
-__device__ __forceinline__ void list_common_bits(SelectLds<BLOCK>& lds, int m, int t, int lane, uint32_t& kor,
-                                                 uint32_t& kand, uint32_t& uor, uint32_t& uand) {
-  uint32_t a = 0u, b = ~0u, c = 0u, d = ~0u;
-  for (int e = t; e < m; e += BLOCK) {
-    const uint2 x = lds.list[e];
-    a |= x.x;
-    b &= x.x;
-    c |= ~x.y;
-    d &= ~x.y;
-  }
+__device__ __forceinline__ void block_common_bits(SelectLds<BLOCK>& lds, int lane, uint32_t a, uint32_t b, uint32_t c,
+                                                  uint32_t d, uint32_t& kor, uint32_t& kand, uint32_t& uor,
+                                                  uint32_t& uand) {
   a = wave_or(a);
   b = wave_and(b);
   c = wave_or(c);
@@ -471,6 +465,21 @@ __device__ __forceinline__ void list_common_bits(SelectLds<BLOCK>& lds, int m, i
   kand = uniform(lds.common[1]);
   uor = uniform(lds.common[2]);
   uand = uniform(lds.common[3]);
+}
+
+// The common bits of the threshold list's keys and complemented ids.
+template <int BLOCK>
+__device__ __forceinline__ void list_common_bits(SelectLds<BLOCK>& lds, int m, int t, int lane, uint32_t& kor,
+                                                 uint32_t& kand, uint32_t& uor, uint32_t& uand) {
+  uint32_t a = 0u, b = ~0u, c = 0u, d = ~0u;
+  for (int e = t; e < m; e += BLOCK) {
+    const uint2 x = lds.list[e];
+    a |= x.x;
+    b &= x.x;
+    c |= ~x.y;
+    d &= ~x.y;
+  }
+  block_common_bits(lds, lane, a, b, c, d, kor, kand, uor, uand);
 }
 
 // Exclusive rank of every flagged item (flag[i] is 0 or 1) among the flagged
@@ -982,28 +991,70 @@ __global__ __launch_bounds__(BLOCK) void stable_topk_kernel(Source src, Sink sin
     }
     dup = tie && ik.count > ik.need;  // identical (key, id) pairs straddle the boundary
   } else if (m != sk.need) {
-    // 3'. a bin too large for the list: the remaining passes over the registers
-    do {
-      radix_pass<BLOCK, 10, 11>(lds, 1, key, valid, sk, t, lane);
-      if (sk.count == sk.need) break;
-      radix_pass<BLOCK, 0, 10>(lds, 2, key, valid, sk, t, lane);
-    } while (false);
+    // 3'. a bin too large for the list (at the threshold of a short row, the
+    // padding keys of its empty slots): the bits shared by all of the bin's
+    // items first, so a bin of identical keys needs no key pass and one of
+    // identical (key, id) pairs no id pass either; then the remaining passes
+    // over the registers, from the highest bit where the values differ
+    const uint32_t d0 = sk.prefix >> 21;
+    uint32_t a = 0u, b = ~0u, c = 0u, e = ~0u;
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const bool in_bin = ((valid >> i) & 1u) && (key[i] >> 21) == d0;
+      a |= in_bin ? key[i] : 0u;
+      b &= in_bin ? key[i] : ~0u;
+      c |= in_bin ? ~idv[i] : 0u;
+      e &= in_bin ? ~idv[i] : ~0u;
+    }
+    uint32_t kor, kand, uor, uand;
+    block_common_bits(lds, lane, a, b, c, e, kor, kand, uor, uand);
+    // register passes run on hist[p % 3] for p = 1, 2, ... in turn (the
+    // rotation that clears each histogram two passes before its next use)
+    int p = 1;
+    if (kor == kand) {  // every item of the bin has the same key
+      sk.prefix = kor;
+      sk.mask = ~0u;
+    } else {
+      do {
+        radix_pass<BLOCK, 10, 11>(lds, p++, key, valid, sk, t, lane);
+        if (sk.count == sk.need) break;
+        radix_pass<BLOCK, 0, 10>(lds, p++, key, valid, sk, t, lane);
+      } while (false);
+    }
     tie = sk.count > sk.need;
     if (tie) {
-      uint32_t u[N], tied = 0;
-#pragma unroll
-      for (int i = 0; i < N; ++i) {
-        u[i] = ~idv[i];
-        tied |= (((valid >> i) & 1u) && key[i] == sk.prefix) ? (1u << i) : 0u;
-      }
+      // the tied items are some of the bin's, so the bits where all of the
+      // bin's ids agree are fixed for them too
       ik.need = sk.need;
-      do {
-        radix_pass<BLOCK, 21, 11>(lds, 3, u, tied, ik, t, lane);
-        if (ik.count == ik.need) break;
-        radix_pass<BLOCK, 10, 11>(lds, 4, u, tied, ik, t, lane);
-        if (ik.count == ik.need) break;
-        radix_pass<BLOCK, 0, 10>(lds, 5, u, tied, ik, t, lane);
-      } while (false);
+      ik.count = sk.count;
+      const uint32_t differ = uor ^ uand;
+      if (differ == 0u) {  // full duplicates: positions decide among them
+        ik.prefix = uand;
+        ik.mask = ~0u;
+      } else {
+        uint32_t u[N], tied = 0;
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+          u[i] = ~idv[i];
+          tied |= (((valid >> i) & 1u) && key[i] == sk.prefix) ? (1u << i) : 0u;
+        }
+        const int hb = 31 - __builtin_clz(differ);
+        if (hb < 31) {
+          ik.mask = ~0u << (hb + 1);
+          ik.prefix = uand & ik.mask;
+        }
+        do {
+          if (hb >= 21) {
+            radix_pass<BLOCK, 21, 11>(lds, p++, u, tied, ik, t, lane);
+            if (ik.count == ik.need) break;
+          }
+          if (hb >= 10) {
+            radix_pass<BLOCK, 10, 11>(lds, p++, u, tied, ik, t, lane);
+            if (ik.count == ik.need) break;
+          }
+          radix_pass<BLOCK, 0, 10>(lds, p++, u, tied, ik, t, lane);
+        } while (false);
+      }
       dup = ik.count > ik.need;
     }
   }

@@ -291,3 +291,29 @@ def test_padding_in_the_threshold_bin(c, k, pad, misalign):
     real_inf = rng.random(s.shape) < 0.02
     s[real_inf] = -np.inf
     assert_select_parity(s, ids, k, f"padding threshold C={c} k={k} pad={pad}", misalign=misalign)
+
+
+@pytest.mark.parametrize("k", [1, 2048, 5000])
+def test_oversized_threshold_bin_common_bits(k):
+    """Threshold bins of more than 2048 items (the register passes): bits that
+    every item of the bin shares are fixed without a pass, so these rows hit
+    each entry point of the key and id passes: identical keys with ids that
+    differ only in their low 9 bits, only below bit 18 and in bit 31; keys
+    that differ with ids that differ in 2 bits; padding mixed with real -inf
+    scores."""
+    rng = np.random.default_rng(4100 + k)
+    rows, c = 6, 8192
+    s = np.full((rows, c), 2.0, np.float32)
+    ids = np.empty((rows, c), np.int32)
+    ids[0] = rng.integers(0, 512, size=c)
+    ids[1] = 0x12340000 + rng.integers(0, 1 << 18, size=c)
+    s[2] = (np.float32(1.0) + rng.random(c, dtype=np.float32) * np.float32(0.0009)).astype(np.float32)
+    ids[2] = 5 + rng.integers(0, 4, size=c)
+    s[3] = -np.inf
+    ids[3] = np.where(rng.random(c) < 0.5, 2**31 - 1, rng.permutation(c)).astype(np.int32)
+    s[4] = -0.0
+    ids[4] = 42
+    ids[4, rng.choice(c, 100, replace=False)] = -42
+    s[5] = 2.0
+    ids[5] = rng.permutation(c)
+    assert_select_parity(s, ids, k, f"oversized threshold bins k={k}")
