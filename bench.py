@@ -54,9 +54,9 @@ def parse_args():
     p.add_argument("--steps", type=int, default=200, help="select launches per timed trial")
     p.add_argument("--warmup", type=int, default=20, help="untimed launches before timing")
     p.add_argument("--trials", type=int, default=7)
-    p.add_argument("--configs", default="large,large_warm,large_eager,decode,tie_heavy,prefill,fused,local",
-                   help="comma list of large_warm, large_eager, decode, tie_heavy, prefill, fused, local; the "
-                        "cold large headline always runs (--configs large runs it alone, as profiled)")
+    p.add_argument("--configs", default="large,large_warm,large_eager,decode,tie_heavy,short_context,prefill,fused,local",
+                   help="comma list of large_warm, large_eager, decode, tie_heavy, short_context, prefill, fused, "
+                        "local; the cold large headline always runs (--configs large runs it alone, as profiled)")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU oracle work to time")
     p.add_argument("--pmc", action="store_true",
@@ -519,6 +519,14 @@ def main():
                                          "cold_candidates_per_s": round(cold["candidates_per_s"]),
                                          "cold_GBps": cold["GBps"], "cold_frac_of_peak": cold["frac_of_peak"]}
         log(f"[tie_heavy] cold {cold['us_per_launch']:.3f} us, warm {hot['us_per_launch']:.3f} us")
+    if "short_context" in configs:
+        gs = W.short_context()
+        cold = bench_select(run, gs, args.steps, args.warmup, args.trials, cold=True)
+        hot = bench_select(run, gs, args.steps, args.warmup, args.trials, cold=False)
+        extra["short_context_latency_us"] = {"rows": gs.rows, "cold_us": round(cold["us_per_launch"], 3),
+                                             "warm_us": round(hot["us_per_launch"], 3),
+                                             "padding_frac": round(float((gs.scores == -float("inf")).mean()), 3)}
+        log(f"[short_context] cold {cold['us_per_launch']:.3f} us, warm {hot['us_per_launch']:.3f} us")
     if "prefill" in configs:
         extra["prefill"] = bench_prefill(run, args.trials)
         log(f"[prefill] {extra['prefill']}")

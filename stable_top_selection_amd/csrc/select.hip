@@ -861,26 +861,26 @@ __global__ __launch_bounds__(BLOCK) void stable_topk_kernel(Source src, Sink sin
       for (int j = 0; j < VEC; ++j) valid |= (first + v * kChunk + j < C) ? 1u << (v * VEC + j) : 0u;
   }
 
-  uint32_t key[N];
-#pragma unroll
-  for (int i = 0; i < N; ++i) key[i] = score_key(bits[i]);
-
   // 2. pass 0: histogram of the top 11 bits; each item keeps its rank in its
   // bin.  Padding keys (-inf: empty shard slots, which can fill whole ranks)
   // would all hit one bin, and LDS atomics to one address serialise, so they
   // count into kPadWords words instead (by lane) and join their bin in the
-  // digit search (and, if that bin is the threshold's, in the list).
+  // digit search (and, if that bin is the threshold's, in the list).  Each
+  // chunk's key transform and atomics stay between scheduling barriers, right
+  // after the wait for that chunk's load, so that pass 0 runs while later
+  // chunks are still arriving (left alone, the compiler hoists every key
+  // transform, and so every load wait, above the first atomic).
+  uint32_t key[N];
   uint32_t rank_in_bin[N];
   uint32_t* pad_word = lds.padcnt + (lane % kPadWords);
-  if constexpr (FULL) {
+  uint32_t* spare = lds.sink + lane;  // target of masked-out items
 #pragma unroll
-    for (int i = 0; i < N; ++i) rank_in_bin[i] = lds_add(key[i] == kPadKey ? pad_word : lds.hist[0] + (key[i] >> 21));
-  } else {
-    uint32_t* sink = lds.sink + lane;
-#pragma unroll
-    for (int i = 0; i < N; ++i)
-      rank_in_bin[i] =
-          lds_add((valid >> i) & 1u ? (key[i] == kPadKey ? pad_word : lds.hist[0] + (key[i] >> 21)) : sink);
+  for (int i = 0; i < N; ++i) {
+    key[i] = score_key(bits[i]);
+    uint32_t* target = key[i] == kPadKey ? pad_word : lds.hist[0] + (key[i] >> 21);
+    if constexpr (!FULL) target = (valid >> i) & 1u ? target : spare;
+    rank_in_bin[i] = lds_add(target);
+    if (i % VEC == VEC - 1) __builtin_amdgcn_sched_barrier(0);
   }
   lds_barrier();
   // padding keys counted in pass 0, in total and in the words before this lane's

@@ -201,6 +201,26 @@ def tie_heavy(rows: int = 16, seed: int = 4) -> Gathered:
                     local_k=local_k, meta={"empty_shards": empty})
 
 
+def short_context(rows: int = 16, seed: int = 8, min_len: int = 64) -> Gathered:
+    """A decode batch whose contexts are shorter than K: row r's context of
+    L_r ~ U[min_len, 2048) tokens is spread over the 4 ranks token by token,
+    so rank j holds ceil((L_r - j) / 4) valid entries at the start of its
+    2048-slot slice and padding after them.  Every real candidate is selected
+    and the threshold falls among the padding."""
+    rng = np.random.default_rng(seed)
+    dcp, local_k = 4, 2048
+    scores = rng.standard_normal((rows, dcp * local_k), dtype=np.float32)
+    ids = _rank_ids(rng, rows, dcp, local_k, 32768)
+    lengths = rng.integers(min_len, local_k, size=rows)
+    for row, length in enumerate(lengths):
+        for r in range(dcp):
+            valid = max(0, -(-(int(length) - r) // dcp))
+            scores[row, r * local_k + valid:(r + 1) * local_k] = PAD_SCORE
+            ids[row, r * local_k + valid:(r + 1) * local_k] = INT32_MAX
+    return Gathered(f"short_context_rows{rows}", np.ascontiguousarray(scores), ids, k=2048, dcp=dcp,
+                    local_k=local_k, meta={"context_lengths": [int(x) for x in lengths]})
+
+
 def prefill(rows: int = 8192, seed: int = 5, dcp: int = 4, local_k: int = 2048,
             invalid_frac: float = 0.0) -> LocalShards:
     """``invalid_frac`` of the local slots, chosen at random after the draws

@@ -1,6 +1,6 @@
 """GPU parity of dcp_topk_select with the CPU oracle: bit-exact scores and ids.
 
-Covers the five workloads at full size, the decode rows sweep, ragged sizes on
+Covers the named workloads at full size, the decode rows sweep, ragged sizes on
 both load paths, the degenerate cases, heavy-tie trials, adversarial floats,
 determinism and guard bands around the output.
 """
@@ -22,7 +22,7 @@ def _gpu():
     B.load_library()
 
 
-@pytest.mark.parametrize("name", ["tiny", "decode", "large", "tie_heavy"])
+@pytest.mark.parametrize("name", ["tiny", "decode", "large", "tie_heavy", "short_context"])
 def test_workloads_full_size(name):
     g = getattr(W, name)()
     print(f"[select parity] {g.name} rows={g.rows} C={g.num_cand} k={g.k} digest={g.digest()}", flush=True)
