@@ -284,9 +284,11 @@ __device__ __forceinline__ void clear_words(uint32_t* p, int words, int t) {
 }
 
 // Register pass p >= 1 over the digit at SHIFT (BITS wide) of the eligible
-// values that match the prefix.  Uses hist[p % 3]; after its barrier clears
-// hist[(p + 2) % 3], which pass p - 1 used and pass p + 2 will use.
-template <int BLOCK, int SHIFT, int BITS, int N>
+// values that match the prefix (the values are ~val[i] when COMPL, so ids are
+// ranked with no complemented copy held in registers).  Uses hist[p % 3];
+// after its barrier clears hist[(p + 2) % 3], which pass p - 1 used and pass
+// p + 2 will use.
+template <int BLOCK, int SHIFT, int BITS, bool COMPL, int N>
 __device__ __forceinline__ void radix_pass(SelectLds<BLOCK>& lds, int pass, const uint32_t (&val)[N],
                                            uint32_t eligible, Radix& st, int t, int lane) {
   constexpr int NB = 1 << BITS;
@@ -297,8 +299,9 @@ __device__ __forceinline__ void radix_pass(SelectLds<BLOCK>& lds, int pass, cons
   // sink word: no per-item branch
 #pragma unroll
   for (int i = 0; i < N; ++i) {
-    const bool counts = ((eligible >> i) & 1u) && (val[i] & st.mask) == st.prefix;
-    lds_add(counts ? hist + ((val[i] >> SHIFT) & kDigitMask) : sink);
+    const uint32_t v = COMPL ? ~val[i] : val[i];
+    const bool counts = ((eligible >> i) & 1u) && (v & st.mask) == st.prefix;
+    lds_add(counts ? hist + ((v >> SHIFT) & kDigitMask) : sink);
   }
   lds_barrier();
   clear_words<BLOCK>(lds.hist[(pass + 2) % 3], kBins, t);
@@ -560,9 +563,10 @@ __device__ __forceinline__ void position_rank(const uint32_t (&flag)[N], uint32_
 // first = w*64*N + VEC*lane.  count(row) is the row's candidate count C (at
 // most the launch's num_cand); the values at positions at or past C are
 // ignored.  load() only issues the reads (into bits/idv and, for per-chunk
-// wave-uniform values, aux); finish() turns what arrived into (score bits, id)
-// after the kernel's first barrier, so that the loads stay in flight while the
-// kernel clears LDS.
+// wave-uniform values, aux); finish<VEC>(v, ...) turns what arrived for chunk
+// v into (score bits, id).  The kernel finishes each chunk just before it
+// first uses it, after its first barrier, so the loads stay in flight while
+// it clears LDS and the work on early chunks overlaps later chunks' arrival.
 // ---------------------------------------------------------------------------
 
 // A row-major gathered candidate buffer: raw buffer loads over the row, the
@@ -573,8 +577,8 @@ struct GatheredSource {
 
   __device__ __forceinline__ int count(int64_t) const { return num_cand; }
 
-  template <int VEC, int NV>
-  __device__ __forceinline__ void finish(const uint32_t*, uint32_t*, uint32_t*) const {}
+  template <int VEC>
+  __device__ __forceinline__ void finish(int, const uint32_t*, uint32_t*, uint32_t*) const {}
 
   template <int VEC, int NV>
   __device__ __forceinline__ void load(int64_t row, int first, int C, uint32_t* bits, uint32_t* idv,
@@ -680,6 +684,9 @@ struct RankSource {
         bits[v] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(sp[v] + at));
         idv[v] = static_cast<uint32_t>(__builtin_nontemporal_load(ip[v] + at));
       }
+      // issue the loads chunk by chunk (scores and indices together), so that
+      // pass 0 can start on chunk 0 as soon as its two loads are back
+      __builtin_amdgcn_sched_barrier(0);
     }
     // the id bases: scalar loads, counted apart from the vector loads, so
     // waiting for them never waits for the data
@@ -688,17 +695,14 @@ struct RankSource {
   }
 
   // bits/idv hold score bits and local indices, aux the chunks' id bases
-  template <int VEC, int NV>
-  __device__ __forceinline__ void finish(const uint32_t* aux, uint32_t* bits, uint32_t* idv) const {
+  template <int VEC>
+  __device__ __forceinline__ void finish(int v, const uint32_t* aux, uint32_t* bits, uint32_t* idv) const {
+    const uint32_t base = aux[v];
 #pragma unroll
-    for (int v = 0; v < NV; ++v) {
-      const uint32_t base = aux[v];
-#pragma unroll
-      for (int j = 0; j < VEC; ++j) {
-        const bool invalid = static_cast<int32_t>(idv[v * VEC + j]) < 0;
-        bits[v * VEC + j] = invalid ? kPadBits : bits[v * VEC + j];
-        idv[v * VEC + j] = invalid ? kPadId : idv[v * VEC + j] + base;
-      }
+    for (int j = 0; j < VEC; ++j) {
+      const bool invalid = static_cast<int32_t>(idv[v * VEC + j]) < 0;
+      bits[v * VEC + j] = invalid ? kPadBits : bits[v * VEC + j];
+      idv[v * VEC + j] = invalid ? kPadId : idv[v * VEC + j] + base;
     }
   }
 };
@@ -717,8 +721,8 @@ struct DenseSource {
     return len < 0 ? 0 : (len < num_cols ? len : num_cols);
   }
 
-  template <int VEC, int NV>
-  __device__ __forceinline__ void finish(const uint32_t*, uint32_t*, uint32_t*) const {}
+  template <int VEC>
+  __device__ __forceinline__ void finish(int, const uint32_t*, uint32_t*, uint32_t*) const {}
 
   template <int VEC, int NV>
   __device__ __forceinline__ void load(int64_t row, int first, int C, uint32_t* bits, uint32_t* idv,
@@ -822,25 +826,19 @@ __global__ __launch_bounds__(BLOCK) void stable_topk_kernel(Source src, Sink sin
   const int C = src.count(row);
   const typename Sink::Row dst = sink.bind(row, k);
 
-  // 1. issue every load of the row before touching LDS.  Wave w reads
-  // positions [w*64*N, (w+1)*64*N), 64*VEC consecutive ones per load.
+  // Wave w reads positions [w*64*N, (w+1)*64*N), 64*VEC consecutive ones per
+  // load.
   const int first = w * kWave * N + VEC * lane;  // this thread's position in chunk 0
   uint32_t bits[N], idv[N], aux[NV];
-  src.template load<VEC, NV>(row, first, C, bits, idv, aux);
 
-  // clear the histograms while the loads are in flight; the key transform
-  // stays after the barrier so that pass 0 starts on the first chunk while
-  // later chunks are still arriving
-  clear_words<BLOCK>(&lds.hist[0][0], 3 * kBins + 3 * kSmallBins + kPadWords, t);
-  if (t < 4) lds.common[t] = (t & 1) ? ~0u : 0u;  // OR slots 0, AND slots ~0 (list_common_bits)
-  lds_barrier();
-  __builtin_amdgcn_sched_barrier(0);
-  src.template finish<VEC, NV>(aux, bits, idv);
-
-  // k >= C: every candidate is selected, in place, then padding
+  // k >= C: every candidate is selected, in place, then padding (a branch
+  // of its own from the start, so that none of its code is shared with, and
+  // hoisted into, the selection path)
   if (k >= C) {
+    src.template load<VEC, NV>(row, first, C, bits, idv, aux);
 #pragma unroll
     for (int v = 0; v < NV; ++v) {
+      src.template finish<VEC>(v, aux, bits, idv);
 #pragma unroll
       for (int j = 0; j < VEC; ++j) {
         const int p = first + v * kChunk + j;
@@ -850,6 +848,17 @@ __global__ __launch_bounds__(BLOCK) void stable_topk_kernel(Source src, Sink sin
     for (int slot = C + t; slot < k; slot += BLOCK) dst.pad(static_cast<uint32_t>(slot));
     return;
   }
+
+  // 1. issue every load of the row before touching LDS
+  src.template load<VEC, NV>(row, first, C, bits, idv, aux);
+
+  // clear the histograms while the loads are in flight; the key transform
+  // stays after the barrier so that pass 0 starts on the first chunk while
+  // later chunks are still arriving
+  clear_words<BLOCK>(&lds.hist[0][0], 3 * kBins + 3 * kSmallBins + kPadWords, t);
+  if (t < 4) lds.common[t] = (t & 1) ? ~0u : 0u;  // OR slots 0, AND slots ~0 (list_common_bits)
+  lds_barrier();
+  __builtin_amdgcn_sched_barrier(0);
 
   // FULL: the row fills every slot (C == BLOCK*N); else the last are masked out
   uint32_t valid = 0xFFFFFFFFu >> (32 - N);
@@ -866,21 +875,21 @@ __global__ __launch_bounds__(BLOCK) void stable_topk_kernel(Source src, Sink sin
   // would all hit one bin, and LDS atomics to one address serialise, so they
   // count into kPadWords words instead (by lane) and join their bin in the
   // digit search (and, if that bin is the threshold's, in the list).  Each
-  // chunk's key transform and atomics stay between scheduling barriers, right
-  // after the wait for that chunk's load, so that pass 0 runs while later
-  // chunks are still arriving (left alone, the compiler hoists every key
-  // transform, and so every load wait, above the first atomic).
+  // chunk is finished, transformed and counted right after the wait for its
+  // own loads, so pass 0 runs while later chunks are still arriving (this
+  // needs the k >= C path to be a branch of its own: code shared with it was
+  // hoisted above its branch, with every load wait).
   uint32_t key[N];
   uint32_t rank_in_bin[N];
   uint32_t* pad_word = lds.padcnt + (lane % kPadWords);
   uint32_t* spare = lds.sink + lane;  // target of masked-out items
 #pragma unroll
   for (int i = 0; i < N; ++i) {
+    if (i % VEC == 0) src.template finish<VEC>(i / VEC, aux, bits, idv);
     key[i] = score_key(bits[i]);
     uint32_t* target = key[i] == kPadKey ? pad_word : lds.hist[0] + (key[i] >> 21);
     if constexpr (!FULL) target = (valid >> i) & 1u ? target : spare;
     rank_in_bin[i] = lds_add(target);
-    if (i % VEC == VEC - 1) __builtin_amdgcn_sched_barrier(0);
   }
   lds_barrier();
   // padding keys counted in pass 0, in total and in the words before this lane's
@@ -894,30 +903,39 @@ __global__ __launch_bounds__(BLOCK) void stable_topk_kernel(Source src, Sink sin
   const uint32_t m = sk.count;  // items in the threshold bin
   bool tie = false, dup = false;
   Radix ik{0u, 0u, 0u, 0u};
-  if (m != sk.need && m <= kListCap) {
-    // 3. the threshold bin as a list: each of its items writes itself at its
-    // pass-0 rank (every other item writes to its lane's dump slot, so the
-    // loop has no per-item branch); then list pass 0 counts the next 8 key
-    // bits
+  // 3. the threshold bin as a list: each of its items writes itself at its
+  // pass-0 rank (every other item writes to its lane's dump slot, so the loop
+  // has no per-item branch).  The list is built in a block of its own, ahead
+  // of the choice between the list passes and the register passes, so that
+  // the pass-0 ranks die before that branch (the scheduling barrier keeps the
+  // compiler from merging the two blocks): each path then fits in 128 VGPRs,
+  // and two 512-thread workgroups share a CU.
+  if (m != sk.need && m <= static_cast<uint32_t>(kListCap)) {
     const uint32_t d0 = sk.prefix >> 21;
-    if (d0 == kPadBin) {
-      // padding keys were ranked per lane: place them after the bin's other
-      // items, lane by lane
-      const uint32_t pw[kPadWords] = {pw0.x, pw0.y, pw0.z, pw0.w, pw1.x, pw1.y, pw1.z, pw1.w};
-      uint32_t before = 0u;
+    if (d0 != kPadBin) {
 #pragma unroll
-      for (int j = 0; j < kPadWords; ++j) before += j < lane % kPadWords ? pw[j] : 0u;
-      const uint32_t pad_base = lds.hist[0][kPadBin] + before;
+      for (int i = 0; i < N; ++i) {
+        const bool in_bin = ((valid >> i) & 1u) && (key[i] >> 21) == d0;
+        lds.list[in_bin ? rank_in_bin[i] : static_cast<uint32_t>(kListCap + lane)] = make_uint2(key[i], idv[i]);
+      }
+    } else {
+      // padding keys were ranked per lane word: they follow the bin's other
+      // items, word by word
+      uint32_t pad_base = lds.hist[0][kPadBin];
 #pragma unroll
-      for (int i = 0; i < N; ++i)
-        if (key[i] == kPadKey) rank_in_bin[i] += pad_base;
-    }
+      for (int j = 0; j < kPadWords; ++j) pad_base += j < lane % kPadWords ? lds.padcnt[j] : 0u;
 #pragma unroll
-    for (int i = 0; i < N; ++i) {
-      const bool in_bin = ((valid >> i) & 1u) && (key[i] >> 21) == d0;
-      lds.list[in_bin ? rank_in_bin[i] : static_cast<uint32_t>(kListCap + lane)] = make_uint2(key[i], idv[i]);
+      for (int i = 0; i < N; ++i) {
+        const bool in_bin = ((valid >> i) & 1u) && (key[i] >> 21) == d0;
+        const uint32_t slot = rank_in_bin[i] + (key[i] == kPadKey ? pad_base : 0u);
+        lds.list[in_bin ? slot : static_cast<uint32_t>(kListCap + lane)] = make_uint2(key[i], idv[i]);
+      }
     }
     lds_barrier();
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  if (m != sk.need && m <= kListCap) {
+    // then list pass 0 counts the next 8 key bits
     const uint2* items = list_pass<BLOCK, 13, 8, false>(lds, 0, m, 0u, sk, t, lane);
     int q = 1;
     bool same_ids_known = false, resolved = false;
@@ -1016,9 +1034,9 @@ __global__ __launch_bounds__(BLOCK) void stable_topk_kernel(Source src, Sink sin
       sk.mask = ~0u;
     } else {
       do {
-        radix_pass<BLOCK, 10, 11>(lds, p++, key, valid, sk, t, lane);
+        radix_pass<BLOCK, 10, 11, false>(lds, p++, key, valid, sk, t, lane);
         if (sk.count == sk.need) break;
-        radix_pass<BLOCK, 0, 10>(lds, p++, key, valid, sk, t, lane);
+        radix_pass<BLOCK, 0, 10, false>(lds, p++, key, valid, sk, t, lane);
       } while (false);
     }
     tie = sk.count > sk.need;
@@ -1032,12 +1050,9 @@ __global__ __launch_bounds__(BLOCK) void stable_topk_kernel(Source src, Sink sin
         ik.prefix = uand;
         ik.mask = ~0u;
       } else {
-        uint32_t u[N], tied = 0;
+        uint32_t tied = 0;
 #pragma unroll
-        for (int i = 0; i < N; ++i) {
-          u[i] = ~idv[i];
-          tied |= (((valid >> i) & 1u) && key[i] == sk.prefix) ? (1u << i) : 0u;
-        }
+        for (int i = 0; i < N; ++i) tied |= (((valid >> i) & 1u) && key[i] == sk.prefix) ? (1u << i) : 0u;
         const int hb = 31 - __builtin_clz(differ);
         if (hb < 31) {
           ik.mask = ~0u << (hb + 1);
@@ -1045,14 +1060,14 @@ __global__ __launch_bounds__(BLOCK) void stable_topk_kernel(Source src, Sink sin
         }
         do {
           if (hb >= 21) {
-            radix_pass<BLOCK, 21, 11>(lds, p++, u, tied, ik, t, lane);
+            radix_pass<BLOCK, 21, 11, true>(lds, p++, idv, tied, ik, t, lane);
             if (ik.count == ik.need) break;
           }
           if (hb >= 10) {
-            radix_pass<BLOCK, 10, 11>(lds, p++, u, tied, ik, t, lane);
+            radix_pass<BLOCK, 10, 11, true>(lds, p++, idv, tied, ik, t, lane);
             if (ik.count == ik.need) break;
           }
-          radix_pass<BLOCK, 0, 10>(lds, p++, u, tied, ik, t, lane);
+          radix_pass<BLOCK, 0, 10, true>(lds, p++, idv, tied, ik, t, lane);
         } while (false);
       }
       dup = ik.count > ik.need;
