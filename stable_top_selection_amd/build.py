@@ -6,6 +6,7 @@
 from __future__ import annotations
 
 import os
+import re
 import shutil
 import subprocess
 import sys
@@ -16,6 +17,9 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libdcptopk.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
+# per-kernel register, scratch, occupancy and LDS figures of the last build,
+# from the compiler's resource-usage remarks
+RESOURCES_PATH = os.path.join(PKG, "libdcptopk.kernels.tsv")
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [
@@ -29,7 +33,45 @@ HIPCC_FLAGS = [
     # no packed fp32 instructions anywhere (the library does no fp32 arithmetic
     # at all; this keeps the compiler from forming them)
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # per-kernel resource usage, recorded next to the library
+    "-Rpass-analysis=kernel-resource-usage",
 ]
+
+_RESOURCE_FIELDS = {"VGPRs": "vgprs", "AGPRs": "agprs", "ScratchSize [bytes/lane]": "scratch_bytes",
+                    "Occupancy [waves/SIMD]": "waves_per_simd", "VGPRs Spill": "vgpr_spill",
+                    "SGPRs Spill": "sgpr_spill", "LDS Size [bytes/block]": "lds_bytes"}
+
+
+def parse_resource_remarks(text: str) -> dict[str, dict[str, int]]:
+    """Kernel name -> resource figures, from hipcc's resource-usage remarks."""
+    kernels: dict[str, dict[str, int]] = {}
+    name = None
+    for line in text.splitlines():
+        if "remark:" not in line or "kernel-resource-usage" not in line:
+            continue
+        body = line.split("remark:", 1)[1].rsplit("[-Rpass-analysis", 1)[0].strip()
+        if body.startswith("Function Name:"):
+            name = body.split(":", 1)[1].strip()
+            kernels[name] = {}
+        elif name is not None and ":" in body:
+            key, value = (x.strip() for x in body.rsplit(":", 1))
+            if key in _RESOURCE_FIELDS and value.isdigit():
+                kernels[name][_RESOURCE_FIELDS[key]] = int(value)
+    return kernels
+
+
+def write_resources(kernels: dict[str, dict[str, int]], path: str = RESOURCES_PATH) -> None:
+    cols = list(_RESOURCE_FIELDS.values())
+    with open(path, "w") as f:
+        f.write("kernel\t" + "\t".join(cols) + "\n")
+        for name in sorted(kernels):
+            f.write(name + "\t" + "\t".join(str(kernels[name].get(c, -1)) for c in cols) + "\n")
+
+
+def read_resources(path: str = RESOURCES_PATH) -> dict[str, dict[str, int]]:
+    with open(path) as f:
+        header = f.readline().rstrip("\n").split("\t")[1:]
+        return {p[0]: dict(zip(header, map(int, p[1:]))) for p in (ln.rstrip("\n").split("\t") for ln in f) if p[0]}
 
 
 def hipcc() -> str:
@@ -52,10 +94,15 @@ def build(verbose: bool = False, extra_flags: list[str] | None = None, out: str 
     if res.returncode != 0:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{res.stdout}\n{res.stderr}")
     noise = "is not a recognized feature for this target"  # host pass of the packed-fp32 switch
-    warnings = [ln for ln in res.stderr.splitlines() if ln.strip() and noise not in ln]
+    # drop the resource remarks and the source excerpts printed under them
+    warnings = [ln for ln in res.stderr.splitlines()
+                if ln.strip() and noise not in ln and "kernel-resource-usage" not in ln
+                and not re.match(r"^\s*\d*\s*\|", ln)]
     if verbose and warnings:
         print("\n".join(warnings), file=sys.stderr)
     os.replace(out + ".tmp", out)
+    if out == LIB_PATH:
+        write_resources(parse_resource_remarks(res.stderr))
     return out
 
 

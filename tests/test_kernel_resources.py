@@ -1,0 +1,73 @@
+"""Register, scratch and occupancy budgets of the built kernels, from the
+compiler's resource-usage remarks that every build records next to the
+library.
+
+The many-row launches (the fused merge over a prefill batch, the chunked
+merge, the local top-K over many rows) rely on two 512-thread workgroups
+sharing a CU, so that one row's selection overlaps the next row's loads: the
+kernels they use must stay within 128 VGPRs (4 waves per SIMD).  Losing that
+halves their throughput with no change in results, which no parity test
+would notice.
+"""
+import os
+import re
+
+import pytest
+
+from stable_top_selection_amd import build as BLD
+
+pytestmark = pytest.mark.skipif(not os.path.exists(BLD.RESOURCES_PATH),
+                                reason="library not built (run __graft_entry__.build())")
+
+SELECT = re.compile(r"stable_topk_kernelILi(\d+)ELi(\d+)ELi(\d+)ELb([01])ENS0_\d+(\w+?Source)")
+
+# (source, items per load) of the 512-thread, 16-item full-row kernels that
+# launches with 16-byte-aligned arrays take: the gathered select, the fused
+# merge and the local top-K
+MANY_ROW_KERNELS = {("GatheredSource", 2), ("RankSource", 4), ("DenseSource", 4)}
+
+
+def _select_kernels():
+    out = []
+    for name, r in BLD.read_resources().items():
+        m = SELECT.search(name)
+        if m:
+            block, vec, n, full, source = int(m[1]), int(m[2]), int(m[3]), m[4] == "1", m[5]
+            out.append((name, block, vec, n, full, source, r))
+    return out
+
+
+def test_every_kernel_reported():
+    kernels = BLD.read_resources()
+    assert sum(1 for n in kernels if "pack_kernel" in n) == 2
+    assert len(_select_kernels()) >= 90
+
+
+def test_many_row_kernels_fit_two_workgroups_per_cu():
+    seen = set()
+    for name, block, vec, n, full, source, r in _select_kernels():
+        if block == 512 and full and (n == 8 or (n == 16 and (source, vec) in MANY_ROW_KERNELS)):
+            seen.add((source, vec, n))
+            assert r["waves_per_simd"] >= 4, f"{name}: {r['vgprs']} VGPRs, {r['waves_per_simd']} waves per SIMD"
+            assert 2 * r["lds_bytes"] <= 160 * 1024, f"{name}: {r['lds_bytes']} B of LDS per workgroup"
+    assert {(s, v, 16) for s, v in MANY_ROW_KERNELS} <= seen
+
+
+def test_no_scratch_up_to_16_items():
+    """No kernel of up to 16 items per thread spills to memory (32-item rows,
+    C above 8192, are allowed the occasional spill)."""
+    for name, block, vec, n, full, source, r in _select_kernels():
+        if n <= 16:
+            assert r["scratch_bytes"] == 0 and r["vgpr_spill"] == 0, f"{name}: {r}"
+    for name, r in BLD.read_resources().items():
+        if "pack_kernel" in name:
+            assert r["scratch_bytes"] == 0, f"{name}: {r}"
+
+
+def test_remark_parser():
+    text = ("a.hip:1:1: remark: Function Name: kern [-Rpass-analysis=kernel-resource-usage]\n"
+            "a.hip:1:1: remark:     VGPRs: 113 [-Rpass-analysis=kernel-resource-usage]\n"
+            "a.hip:1:1: remark:     Occupancy [waves/SIMD]: 4 [-Rpass-analysis=kernel-resource-usage]\n"
+            "a.hip:1:1: remark:     LDS Size [bytes/block]: 77680 [-Rpass-analysis=kernel-resource-usage]\n"
+            "    1 | int x;\n")
+    assert BLD.parse_resource_remarks(text) == {"kern": {"vgprs": 113, "waves_per_simd": 4, "lds_bytes": 77680}}
