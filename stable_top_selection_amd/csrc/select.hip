@@ -270,8 +270,8 @@ struct alignas(16) SelectLds {
   uint32_t hist[3][kBins];         // pass 0 (hist[0]) and the register passes, rotating
   uint32_t small[3][kSmallBins];   // list passes, rotating
   uint32_t padcnt[kPadWords];      // pass 0: counts of padding keys, by lane % kPadWords
-  uint2 list[kListCap + kWave];    // (key, id) of the items in the pass-0 threshold bin, then
-                                   // one write-only dump slot per lane
+  uint2 list[kListCap + 1];        // (key, id) of the items in the pass-0 threshold bin, then
+                                   // one write-only dump slot for all other items
   uint32_t segment[2][kWaves];     // per-wave flagged counts (dup scan, select scan)
   uint32_t sink[kWave];            // per-lane target of atomics whose item does not count
   uint32_t common[4];              // OR / AND of the list's keys and of its complemented ids
@@ -310,6 +310,11 @@ __device__ __forceinline__ void radix_pass(SelectLds<BLOCK>& lds, int pass, cons
 
 // List pass q over the digit at SHIFT (BITS wide): score keys of the list
 // (BY_ID false) or complemented ids of the list items whose key is `thr`.
+// ALL: every list item matches (the first key pass, whose list holds exactly
+// the items of the pass-0 threshold bin), so no item is tested and each reads
+// its (key, id) pair in one LDS load; an item past its digit's bucket writes
+// to a dump slot (the first word after the buckets, in hist[2], which no list
+// path uses) instead of branching.
 // Counts into small[q % 3] and, after its barrier, clears small[(q + 2) % 3]
 // (used by pass q - 1, next used by pass q + 2).  The pass also sorts the list
 // coarsely: each counted item's atomic returns its rank inside its digit, and
@@ -320,18 +325,23 @@ __device__ __forceinline__ void radix_pass(SelectLds<BLOCK>& lds, int pass, cons
 // barrier.  The buckets overlay the pass-0 histograms, which every wave has
 // finished reading before the list build's barrier; each pass overwrites the
 // previous pass's buckets, which are read only when no further pass follows.
-template <int BLOCK, int SHIFT, int BITS, bool BY_ID>
+template <int BLOCK, int SHIFT, int BITS, bool BY_ID, bool ALL = false>
 __device__ __forceinline__ const uint2* list_pass(SelectLds<BLOCK>& lds, int q, int m, uint32_t thr, Radix& st,
                                                   int t, int lane) {
   constexpr int NB = 1 << BITS;
   constexpr uint32_t kDigitMask = NB - 1;
-  static_assert(sizeof(lds.hist) >= NB * kBucket * sizeof(uint2), "buckets fit");
+  static_assert(sizeof(lds.hist) >= (NB * kBucket + 1) * sizeof(uint2), "buckets and the dump slot fit");
+  static_assert(!ALL || !BY_ID, "only the first key pass takes every item");
   uint32_t* hist = lds.small[q % 3];
   uint2* bucket = reinterpret_cast<uint2*>(&lds.hist[0][0]);
   for (int e = t; e < m; e += BLOCK) {
     const uint2 x = lds.list[e];
     const uint32_t v = BY_ID ? ~x.y : x.x;
-    if ((!BY_ID || x.x == thr) && (v & st.mask) == st.prefix) {
+    if constexpr (ALL) {
+      const uint32_t d = (v >> SHIFT) & kDigitMask;
+      const uint32_t r = lds_add(hist + d);
+      bucket[r < static_cast<uint32_t>(kBucket) ? d * kBucket + r : NB * kBucket] = make_uint2(x.x, ~x.y);
+    } else if ((!BY_ID || x.x == thr) && (v & st.mask) == st.prefix) {
       const uint32_t d = (v >> SHIFT) & kDigitMask;
       const uint32_t r = lds_add(hist + d);
       if (r < static_cast<uint32_t>(kBucket)) bucket[d * kBucket + r] = make_uint2(x.x, ~x.y);
@@ -814,8 +824,9 @@ __global__ __launch_bounds__(BLOCK) void stable_topk_kernel(Source src, Sink sin
   constexpr int NV = N / VEC;
   constexpr int kChunk = VEC * kWave;  // consecutive positions per chunk and wave
   __shared__ SelectLds<BLOCK> lds;
-  // per-wave output staging: half of a wave's slots, at most 448, plus one
-  // spare slot per lane
+  // per-wave output staging: half of a wave's slots, at most 448, then one
+  // write-only spare slot (the area has kWave slots past kStageCap so that the
+  // wave's whole-row copy-out reads stay inside it when kStageCap < 64)
   constexpr int kStageCap = kWave * N / 2 < 448 ? kWave * N / 2 : 448;
   __shared__ uint2 stage[BLOCK / kWave][kStageCap + kWave];
 
@@ -904,7 +915,7 @@ __global__ __launch_bounds__(BLOCK) void stable_topk_kernel(Source src, Sink sin
   bool tie = false, dup = false;
   Radix ik{0u, 0u, 0u, 0u};
   // 3. the threshold bin as a list: each of its items writes itself at its
-  // pass-0 rank (every other item writes to its lane's dump slot, so the loop
+  // pass-0 rank (every other item writes to one shared dump slot, so the loop
   // has no per-item branch).  The list is built in a block of its own, ahead
   // of the choice between the list passes and the register passes, so that
   // the pass-0 ranks die before that branch (the scheduling barrier keeps the
@@ -916,7 +927,7 @@ __global__ __launch_bounds__(BLOCK) void stable_topk_kernel(Source src, Sink sin
 #pragma unroll
       for (int i = 0; i < N; ++i) {
         const bool in_bin = ((valid >> i) & 1u) && (key[i] >> 21) == d0;
-        lds.list[in_bin ? rank_in_bin[i] : static_cast<uint32_t>(kListCap + lane)] = make_uint2(key[i], idv[i]);
+        lds.list[in_bin ? rank_in_bin[i] : static_cast<uint32_t>(kListCap)] = make_uint2(key[i], idv[i]);
       }
     } else {
       // padding keys were ranked per lane word: they follow the bin's other
@@ -928,7 +939,7 @@ __global__ __launch_bounds__(BLOCK) void stable_topk_kernel(Source src, Sink sin
       for (int i = 0; i < N; ++i) {
         const bool in_bin = ((valid >> i) & 1u) && (key[i] >> 21) == d0;
         const uint32_t slot = rank_in_bin[i] + (key[i] == kPadKey ? pad_base : 0u);
-        lds.list[in_bin ? slot : static_cast<uint32_t>(kListCap + lane)] = make_uint2(key[i], idv[i]);
+        lds.list[in_bin ? slot : static_cast<uint32_t>(kListCap)] = make_uint2(key[i], idv[i]);
       }
     }
     lds_barrier();
@@ -936,7 +947,7 @@ __global__ __launch_bounds__(BLOCK) void stable_topk_kernel(Source src, Sink sin
   __builtin_amdgcn_sched_barrier(0);
   if (m != sk.need && m <= kListCap) {
     // then list pass 0 counts the next 8 key bits
-    const uint2* items = list_pass<BLOCK, 13, 8, false>(lds, 0, m, 0u, sk, t, lane);
+    const uint2* items = list_pass<BLOCK, 13, 8, false, true>(lds, 0, m, 0u, sk, t, lane);
     int q = 1;
     bool same_ids_known = false, resolved = false;
     uint32_t uor = 0u, uand = 0u;
@@ -1107,7 +1118,7 @@ __global__ __launch_bounds__(BLOCK) void stable_topk_kernel(Source src, Sink sin
   // 5. stable compaction and store.  Wave w's selected items fill the output
   // slots [out_first, out_first + out_count) (its positions precede all later
   // waves'), so each wave stages its own items in its own LDS area at their
-  // rank inside the wave (unselected items write to this lane's spare slot, so
+  // rank inside the wave (unselected items write to the area's spare slot, so
   // the loop has no per-item branch) while the waves' counts are exchanged,
   // then writes its range with consecutive stores.  A wave with more selected
   // items than its area stores every item at its rank from the registers.
@@ -1118,7 +1129,7 @@ __global__ __launch_bounds__(BLOCK) void stable_topk_kernel(Source src, Sink sin
   if (staged) {
 #pragma unroll
     for (int i = 0; i < N; ++i) {
-      const uint32_t slot = sel[i] ? rank[i] : static_cast<uint32_t>(kStageCap + lane);
+      const uint32_t slot = sel[i] ? rank[i] : static_cast<uint32_t>(kStageCap);
       stage[w][slot] = make_uint2(bits[i], idv[i]);
     }
   }
