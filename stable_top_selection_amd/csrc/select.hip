@@ -631,9 +631,10 @@ struct GatheredSource {
 // a negative local index is the padding candidate (vLLM PR #59367, Purpose).
 // local_k is a multiple of 64*VEC, so a chunk never straddles two ranks and a
 // chunk's rank is wave-uniform.  A wave reads its chunks' rank-table entries
-// (scalar loads) before its first data load and the row starts (scalar loads
-// too) after its last, so that the data loads go out back to back and the
-// pack arithmetic waits only for its own operands.
+// and then their row starts (scalar loads) before its first data load, so the
+// id bases are back by the time the first chunk arrives (measured against
+// reading the row starts after the last data load: 256 rows 8.14 -> 8.02 us,
+// 8192 rows 134.5 -> 132.2 us).
 struct RankSource {
   static constexpr bool kChunkLoads = false;  // a wave's loads go out together (see load)
   FusedRanks ranks;
@@ -680,6 +681,8 @@ struct RankSource {
       off[v] = static_cast<uint32_t>(pr.rank_offset);
     }
 #pragma unroll
+    for (int v = 0; v < NV; ++v) aux[v] = static_cast<uint32_t>(rp[v][row]) + off[v];
+#pragma unroll
     for (int v = 0; v < NV; ++v) {
       const int64_t at = row * local_k + j0[v] + lane_off;
       if constexpr (VEC == 4) {
@@ -708,10 +711,6 @@ struct RankSource {
       // pass 0 can start on chunk 0 as soon as its two loads are back
       __builtin_amdgcn_sched_barrier(0);
     }
-    // the id bases: scalar loads, counted apart from the vector loads, so
-    // waiting for them never waits for the data
-#pragma unroll
-    for (int v = 0; v < NV; ++v) aux[v] = static_cast<uint32_t>(rp[v][row]) + off[v];
   }
 
   // bits/idv hold score bits and local indices, aux the chunks' id bases
