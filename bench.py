@@ -541,6 +541,13 @@ def main():
     if not args.no_cpu:
         cpu = cpu_baseline(g, args.cpu_seconds)
         log(f"[cpu oracle] {cpu['value']:.3e} candidates/s ({cpu['sample']})")
+        # the same oracle on the decode and tie-heavy batches (about 2 s each)
+        others = {}
+        for name, go in (("decode_rows16", W.decode(16)), ("tie_heavy", W.tie_heavy())):
+            c = cpu_baseline(go, min(2.0, args.cpu_seconds))
+            others[name] = {"candidates_per_s": round(c["value"]), "cores": c["cores"], "sample": c["sample"]}
+            log(f"[cpu oracle] {name}: {c['value']:.3e} candidates/s ({c['sample']})")
+        extra["cpu_oracle_other_batches"] = others
 
     traffic = traffic_record(us)
     line = {
