@@ -39,10 +39,17 @@ def _p(x):
 
 
 def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
-    """Load libdcptopk.so and declare its signatures (raises if it is missing)."""
+    """Load libdcptopk.so and declare its signatures (raises if it is missing).
+    Every wrapper below calls through the library loaded here."""
     global _lib
-    if _lib is not None:
-        return _lib
+    if _lib is None:
+        _lib = open_library(path)
+    return _lib
+
+
+def open_library(path: str) -> ctypes.CDLL:
+    """Open a build of the library at `path` with its signatures declared,
+    without making it the one the wrappers use."""
     if not os.path.exists(path):
         raise RuntimeError(f"{path} is missing: build it with `python -m stable_top_selection_amd.build`")
     lib = ctypes.CDLL(path)
@@ -61,7 +68,6 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.dcp_topk_local.restype = ctypes.c_int
     lib.dcp_topk_status_string.argtypes = [ctypes.c_int]
     lib.dcp_topk_status_string.restype = ctypes.c_char_p
-    _lib = lib
     return lib
 
 

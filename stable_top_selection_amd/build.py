@@ -17,6 +17,10 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libdcptopk.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
+# the same library with every odd wave delayed after each workgroup barrier
+# (DCPTOPK_RACE_STRESS), for the race-stress tests only
+STRESS_LIB_PATH = os.path.join(PKG, "libdcptopk_race_stress.so")
+STRESS_FLAGS = ["-DDCPTOPK_RACE_STRESS=1"]
 # per-kernel register, scratch, occupancy and LDS figures of the last build,
 # from the compiler's resource-usage remarks
 RESOURCES_PATH = os.path.join(PKG, "libdcptopk.kernels.tsv")
@@ -106,5 +110,15 @@ def build(verbose: bool = False, extra_flags: list[str] | None = None, out: str 
     return out
 
 
+def build_all(verbose: bool = False) -> list[str]:
+    """Both libraries (product and race-stress test build), compiled concurrently."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    with ThreadPoolExecutor(max_workers=2) as pool:
+        main = pool.submit(build, verbose)
+        stress = pool.submit(build, False, STRESS_FLAGS, STRESS_LIB_PATH)
+        return [main.result(), stress.result()]
+
+
 if __name__ == "__main__":
-    print(build(verbose=True))
+    print("\n".join(build_all(verbose=True)))

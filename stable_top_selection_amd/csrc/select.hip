@@ -93,12 +93,28 @@ constexpr uint32_t kPadKey = 0x007FFFFFu;   // the score key of -inf
 constexpr uint32_t kPadBin = kPadKey >> 21; // its pass-0 bin
 constexpr int kPadWords = 8;                // pass-0 counters of padding keys
 
+// Race-stress build (a separate test library compiled with
+// DCPTOPK_RACE_STRESS=1): every odd wave sleeps for tens of microseconds after
+// each workgroup barrier, so it reads shared LDS long after the even waves have
+// gone on to the next phase's writes, clears and reuse of buffers.  If any
+// buffer were reused without a barrier after its last read (the race of the
+// pages' review comment), the delayed waves would read the new contents and the
+// result would differ from the oracle.
+#ifndef DCPTOPK_RACE_STRESS
+#define DCPTOPK_RACE_STRESS 0
+#endif
+
 // LDS-only workgroup barrier: waits for this wave's LDS traffic, not for its
 // outstanding global loads, so the row's loads stay in flight across it.
 __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+  if constexpr (DCPTOPK_RACE_STRESS != 0) {
+    if ((__builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x)) >> 6) & 1) {
+      for (int i = 0; i < 4; ++i) __builtin_amdgcn_s_sleep(127);  // about 32k cycles
+    }
+  }
 }
 
 __device__ __forceinline__ uint32_t lane_of(uint32_t x, int lane) {

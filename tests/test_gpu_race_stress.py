@@ -1,0 +1,88 @@
+"""Race stress: the selection under adversarial wave timing.
+
+vLLM PR #47348 (review comment) describes the race a radix selector must
+avoid: a threshold broadcast through shared memory that is cleared for the next
+phase before every wave has read it, so that late waves drop every tied
+candidate.  These tests run the stress build of the library
+(``DCPTOPK_RACE_STRESS=1``), in which every odd wave sleeps for tens of
+microseconds after each workgroup barrier.  The even waves then move on to the
+next phase's writes, clears and buffer reuse long before the odd waves read
+what the barrier published, so a buffer reused without a barrier after its last
+read would give a wrong result.  Every case must still match the oracle bit
+for bit: the tie-heavy workload on 256 rows, the large workload, padding-heavy
+rows, the register passes (one shared key), full duplicates (the position
+rank), 32 items per thread, the fused merge and the local top-K.
+"""
+import numpy as np
+import pytest
+import torch
+
+from gpu_helpers import assert_select_parity, to_dev
+from oracle import stable_topk as O
+from stable_top_selection_amd import binding as B
+from stable_top_selection_amd import build as BLD
+from stable_top_selection_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _stress_library():
+    """Every binding call in this module goes through the stress build."""
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    product = B.load_library()
+    B._lib = B.open_library(BLD.STRESS_LIB_PATH)
+    yield
+    B._lib = product
+
+
+def _select(g, label):
+    print(f"[race stress] {label}: {g.name} rows={g.rows} C={g.num_cand} k={g.k}", flush=True)
+    assert_select_parity(g.scores, g.ids, g.k, f"race stress {label}", guard=1)
+
+
+@pytest.mark.parametrize("seed", [40, 41])
+def test_tie_heavy_rows(seed):
+    _select(W.tie_heavy(rows=256, seed=seed), "tie-heavy")
+
+
+def test_large_workload():
+    _select(W.large(), "large")
+
+
+def test_padding_heavy_rows():
+    _select(W.short_context(), "short context")
+
+
+@pytest.mark.parametrize("rows,c,k,dist,kw", [
+    (8, 8192, 2048, "const", {}),                                     # one key: register passes
+    (8, 8192, 2048, "const", {"id_span": 64, "repeat_ids": True}),  # full duplicates: position rank
+    (4, 16384, 5000, "levels", {}),                                 # 32 items per thread
+    (5, 2049, 1000, "levels", {}),
+    (3, 1025, 1, "special", {}),
+])
+def test_ragged_and_degenerate(rows, c, k, dist, kw):
+    _select(W.random_gathered(rows, c, k, seed=900 + c + k, dist=dist, **kw), f"{dist} {kw}")
+
+
+def test_fused_merge():
+    sh = W.fused()
+    print(f"[race stress] fused merge {sh.name}", flush=True)
+    sc = [to_dev(sh.scores[r]) for r in range(sh.dcp)]
+    ix = [to_dev(sh.local_idx[r]) for r in range(sh.dcp)]
+    rs = [to_dev(sh.row_starts[r]) for r in range(sh.dcp)]
+    out = B.merge_fused(sc, ix, rs, [int(x) for x in sh.rank_offsets], sh.k)
+    torch.cuda.synchronize()
+    o = out.cpu().numpy()
+    want_s, want_i = O.merge(sh.scores, sh.local_idx, sh.row_starts, sh.rank_offsets, sh.k)
+    assert np.array_equal(o[..., 0].view(np.uint32), want_s.view(np.uint32)) and np.array_equal(o[..., 1], want_i)
+
+
+def test_local_topk():
+    d = W.local(rows=64, dist="levels", with_lengths=True)
+    print(f"[race stress] local top-K {d.name}", flush=True)
+    os_, oi = B.local_topk(to_dev(d.scores), d.k, lengths=to_dev(d.lengths))
+    torch.cuda.synchronize()
+    ws, wi = O.local_topk(d.scores, d.k, d.lengths)
+    assert np.array_equal(os_.cpu().numpy().view(np.uint32), ws.view(np.uint32))
+    assert np.array_equal(oi.cpu().numpy(), wi)
