@@ -9,7 +9,7 @@ import pytest
 
 from oracle import stable_topk as O
 from stable_top_selection_amd import binding as B
-from stable_top_selection_amd.build import LIB_PATH
+from stable_top_selection_amd.build import LIB_PATH, STRESS_LIB_PATH
 
 P = ctypes.c_void_p
 DEV_A = 0x7F0000000000  # fake, 256-byte aligned device addresses: never dereferenced
@@ -31,6 +31,18 @@ def test_exports_every_header_function(lib):
     exported = subprocess.run(["nm", "-D", "--defined-only", LIB_PATH], capture_output=True, text=True).stdout
     public = sorted(line.split()[-1] for line in exported.splitlines() if " T dcp_topk_" in line)
     assert public == names
+
+
+def test_race_stress_build_exports_the_same_functions():
+    """The race-stress build (the GPU race tests load it) is the same library
+    with delayed waves: same entry points, same signatures."""
+    stress = B.open_library(STRESS_LIB_PATH)
+    names = B.header_functions()
+    for n in names:
+        assert hasattr(stress, n), n
+    exported = subprocess.run(["nm", "-D", "--defined-only", STRESS_LIB_PATH], capture_output=True, text=True).stdout
+    assert sorted(line.split()[-1] for line in exported.splitlines() if " T dcp_topk_" in line) == names
+    assert stress.dcp_topk_status_string(0) == b"ok"
 
 
 def test_status_strings(lib):
