@@ -10,7 +10,10 @@ Timing follows the pages' selector microbenchmark (PR #47348, Benchmarks:
 median over 7 trials of 200 launches, warm-up excluded).  The launches of a
 trial are captured once in a HIP graph and replayed, so the per-launch time is
 the GPU's and not the host's launch rate; HIP events on the replay stream
-bracket every trial.  Inputs rotate through a pool larger than twice the
+bracket every trial.  A trial is at least 200 launches whatever ``--steps``
+asks (more when the input pool is larger), so that the graph's own launch
+cost is spread as in the pages' method; the JSON's ``steps`` is the number of
+launches actually timed (trials x launches per trial).  Inputs rotate through a pool larger than twice the
 MI355X's Infinity Cache plus L2 (2 x (256 + 32) MiB), so every launch reads its
 candidates from HBM ("cold").  Warm-cache numbers (one buffer reused) are
 reported separately and labelled.
@@ -39,6 +42,7 @@ METRIC = "select µs/launch + candidates/s and % peak HBM BW (rows=256, 8192 can
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, AMD published peak
 MIB = 1 << 20
 COLD_POOL_BYTES = 2 * (256 + 32) * MIB  # 2 x (Infinity Cache + 8 x 4 MiB L2)
+MIN_LAUNCHES = 200  # launches per timed trial, at least (PR #47348, Benchmarks: 7 x 200)
 CAND_BYTES = 8
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "select_large_rows256_traffic.json")
 SELECT_SOURCE = os.path.join(ROOT, "stable_top_selection_amd", "csrc", "select.hip")
@@ -51,7 +55,8 @@ def log(*a):
 def parse_args():
     p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=200, help="select launches per timed trial")
+    p.add_argument("--steps", type=int, default=200,
+                   help="select launches per timed trial (at least 200 are timed, a whole number of pool passes)")
     p.add_argument("--warmup", type=int, default=20, help="untimed launches before timing")
     p.add_argument("--trials", type=int, default=7)
     p.add_argument("--configs", default="large,large_warm,large_eager,decode,tie_heavy,short_context,prefill,fused,local",
@@ -155,13 +160,20 @@ def check_pool_outputs(run, tensors, gathered, k, sample):
     return len(idx)
 
 
+def launches_per_trial(steps, pool):
+    """At least MIN_LAUNCHES and ``steps`` launches, a whole number of passes
+    over an input pool of ``pool`` buffers."""
+    want = max(MIN_LAUNCHES, steps)
+    return -(-want // pool) * pool
+
+
 def bench_select(run, g, steps, warmup, trials, cold=True):
     """Median per-launch microseconds of a graph of launches rotating over a cold pool."""
     inter = g.interleaved()
     pool_bytes = COLD_POOL_BYTES if cold else 0
     ptrs, tensors = make_pool(run, inter, g.k, pool_bytes)
     n = len(ptrs)
-    launches = max(steps, n) if cold else steps
+    launches = launches_per_trial(steps, n)
     rows, c, k = g.rows, g.num_cand, g.k
 
     def fn(i):
@@ -246,30 +258,50 @@ def bench_prefill(run, trials):
     o = out.cpu().numpy()[rows]
     if not (np.array_equal(o[..., 0].view(np.uint32), want_s.view(np.uint32)) and np.array_equal(o[..., 1], want_i)):
         raise AssertionError("prefill merge differs from the oracle on sampled rows")
-    # select alone on the 8 chunk-sized gathered buffers the merge builds
+    # select alone on the 8 chunk-sized gathered buffers the merge builds (the
+    # workspace is MALL-resident, as it is when the merge's select reads what
+    # its pack just wrote)
     gathered = ws.view(torch.int32).view(min(T, 1024), dcp * lk, 2)
     chunk_outs = [out[c0:c0 + 1024] for c0 in range(0, T, 1024)]
     sel = [lambda spp, o_=o_: run.select(gathered.data_ptr(), 1024, dcp * lk, k, o_.data_ptr(), spp)
            for o_ in chunk_outs]
     g2 = run.graph_of(sel)
     ms_sel = run.time_graph(g2, trials)
+    # pack alone: dcp_topk_pack of every rank of every chunk into the
+    # workspace (one rank per launch; the chunked driver packs all ranks of a
+    # chunk in one launch of the same kernel)
+    ws_ptr = ws.data_ptr()
+
+    def pack_launch(c0, r):
+        n = min(1024, T - c0)
+
+        def f(spp):
+            st = run.lib.dcp_topk_pack(sc[r].data_ptr() + 4 * c0 * lk, ix[r].data_ptr() + 4 * c0 * lk, lk,
+                                       rs[r].data_ptr() + 4 * c0, offs[r], n, lk, ws_ptr + 8 * r * lk, dcp * lk, spp)
+            if st != 0:
+                raise RuntimeError(run.B.status_string(st))
+        return f
+
+    g3 = run.graph_of([pack_launch(c0, r) for c0 in range(0, T, 1024) for r in range(dcp)])
+    ms_pack = run.time_graph(g3, trials)
     merge_ms = statistics.median(ms)
     sel_ms = statistics.median(ms_sel)
+    pack_ms = statistics.median(ms_pack)
     chunks = -(-T // 1024)
     sel_bytes = chunks * select_bytes(1024, dcp * lk, k)
-    pack_bytes = chunks * dcp * 1024 * lk * (4 + 4 + 8) + dcp * T * 4
-    pack_ms = merge_ms - sel_ms
+    pack_bytes = T * dcp * lk * (4 + 4 + 8) + dcp * T * 4
     gb = lambda b, t_ms: b / (t_ms * 1e-3) / 1e9  # noqa: E731
     return {"workload": f"prefill chunked: T={T}, DCP {dcp} x local K {lk}, K {k}, 1024-row chunks",
             "merge_ms": round(merge_ms, 4), "merge_trials_ms": [round(x, 4) for x in ms],
-            "select_only_ms": round(sel_ms, 4), "pack_ms_by_difference": round(pack_ms, 4),
-            "per_chunk_select_us": round(1e3 * sel_ms / chunks, 2), "per_chunk_pack_us": round(1e3 * pack_ms / chunks, 2),
             "merge_GBps": round(gb(sel_bytes + pack_bytes, merge_ms), 1),
-            "select_GBps_L2_warm_workspace": round(gb(sel_bytes, sel_ms), 1),
+            "merge_candidates_per_s": round(T * dcp * lk / (merge_ms * 1e-3)),
+            "select_only_ms": round(sel_ms, 4), "per_chunk_select_us": round(1e3 * sel_ms / chunks, 2),
+            "select_GBps_MALL_resident_workspace": round(gb(sel_bytes, sel_ms), 1),
             "select_frac_of_peak": round(gb(sel_bytes, sel_ms) / PEAK_HBM_GBS, 4),
+            "pack_only_ms": round(pack_ms, 4), "pack_launches": chunks * dcp,
             "pack_GBps": round(gb(pack_bytes, pack_ms), 1),
             "pack_frac_of_peak": round(gb(pack_bytes, pack_ms) / PEAK_HBM_GBS, 4),
-            "merge_candidates_per_s": round(T * dcp * lk / (merge_ms * 1e-3)),
+            "pack_algorithmic_bytes": pack_bytes,
             "rows_checked": int(len(rows))}
 
 
@@ -322,7 +354,7 @@ def bench_fused(run, steps, warmup, trials):
 
     for i in range(warmup):
         launch(i)(run.stream_ptr())
-    launches = max(steps, n)
+    launches = launches_per_trial(steps, n)
     graph = run.graph_of([launch(i) for i in range(launches)])
     ms = run.time_graph(graph, trials)
     us = statistics.median([1e3 * m / launches for m in ms])
@@ -377,57 +409,138 @@ def bench_local(run, steps, warmup, trials):
 
     torch = run.torch
     res = {}
-    for rows, cold in ((64, True), (64, False), (256, True)):
-        d = W.local(rows=rows)
+    for rows, cold, lengths in ((64, True, False), (64, False, False), (256, True, False), (64, True, True),
+                                (256, True, True)):
+        d = W.local(rows=rows, with_lengths=lengths)
         cols, k = d.num_cols, d.k
         per = rows * cols * 4 + rows * k * 8
         n = max(1, -(-COLD_POOL_BYTES // per)) if cold else 1
         src = torch.from_numpy(d.scores).to(run.dev).unsqueeze(0).repeat(n, 1, 1)
         os_ = torch.empty((n, rows, k), dtype=torch.float32, device=run.dev)
         oi = torch.empty((n, rows, k), dtype=torch.int32, device=run.dev)
+        lens = torch.from_numpy(d.lengths).to(run.dev) if lengths else None
+        lens_ptr = lens.data_ptr() if lengths else None
 
         def launch(i):
             def f(sp):
-                st = run.lib.dcp_topk_local(src[i % n].data_ptr(), cols, None, rows, cols, k, os_[i % n].data_ptr(),
-                                            oi[i % n].data_ptr(), k, sp)
+                st = run.lib.dcp_topk_local(src[i % n].data_ptr(), cols, lens_ptr, rows, cols, k,
+                                            os_[i % n].data_ptr(), oi[i % n].data_ptr(), k, sp)
                 if st != 0:
                     raise RuntimeError(run.B.status_string(st))
             return f
 
         for i in range(warmup):
             launch(i)(run.stream_ptr())
-        launches = max(steps, n)
+        launches = launches_per_trial(steps, n)
         graph = run.graph_of([launch(i) for i in range(launches)])
         us = statistics.median([1e3 * m / launches for m in run.time_graph(graph, trials)])
-        ws, wi = oracle.local_topk(d.scores, k)
+        ws, wi = oracle.local_topk(d.scores, k, d.lengths)
         for i in (0, n - 1):
             if not (np.array_equal(os_[i].cpu().numpy().view(np.uint32), ws.view(np.uint32))
                     and np.array_equal(oi[i].cpu().numpy(), wi)):
                 raise AssertionError(f"local top-K output differs from the oracle ({d.name})")
-        res[f"rows{rows}_{'cold' if cold else 'warm'}"] = {
+        res[f"rows{rows}_{'cold' if cold else 'warm'}{'_lengths' if lengths else ''}"] = {
             "us_per_launch": round(us, 3), "GBps": round(per / (us * 1e-6) / 1e9, 1), "pool_buffers": n,
             "algorithmic_bytes_per_launch": per}
-        del graph, src, os_, oi
+        del graph, src, os_, oi, lens
         torch.cuda.empty_cache()
-    res["workload"] = "local top-K: 4096 fp32 columns per row, k 2048, scores N(0,1)"
+    res["workload"] = ("local top-K: 4096 fp32 columns per row, k 2048, scores N(0,1); '_lengths' lines take "
+                       "per-row lengths U[0, 4096] (the partial-row kernels)")
     return res
 
 
-def cpu_baseline(g, seconds):
-    """The CPU oracle (numpy, single-threaded sort) on the same workload."""
+# Arrays the CPU-baseline workers read.  The pool forks before this process
+# touches the GPU, so the workers share them copy-on-write and never hold any
+# GPU state.
+_CPU = {}
+
+
+def _cpu_select_rows(bounds):
+    """One worker's share of a batch: the oracle on rows [lo, hi)."""
     from oracle import stable_topk as oracle
 
+    lo, hi = bounds
+    s, i = oracle.select(_CPU["scores"][lo:hi], _CPU["ids"][lo:hi], _CPU["k"])
+    return int(i[:, :4].astype("int64").sum())  # a checksum: the results stay in the worker
+
+
+def _cpu_merge_rows(bounds):
+    """One worker's share of the prefill merge: pack + select of rows [lo, hi)."""
+    from oracle import stable_topk as oracle
+
+    lo, hi = bounds
+    sh = _CPU["shards"]
+    s, i = oracle.merge(sh.scores[:, lo:hi], sh.local_idx[:, lo:hi], sh.row_starts[:, lo:hi], sh.rank_offsets,
+                        sh.k)
+    return int(i[:, :4].astype("int64").sum())
+
+
+def _blocks(rows, parts):
+    step = -(-rows // parts)
+    return [(lo, min(rows, lo + step)) for lo in range(0, rows, step)]
+
+
+def _timed_runs(fn, seconds, min_runs=3):
     times = []
     t_end = time.perf_counter() + seconds
-    while len(times) < 3 or time.perf_counter() < t_end:
+    while len(times) < min_runs or time.perf_counter() < t_end:
         t0 = time.perf_counter()
-        oracle.select(g.scores, g.ids, g.k)
+        fn()
         times.append(time.perf_counter() - t0)
-    t = statistics.median(times)
-    return {"value": g.rows * g.num_cand / t, "unit": "candidates/s", "cores": 1, "kind": "oracle",
+    return times
+
+
+def cpu_baselines(seconds):
+    """The CPU oracle (numpy, one sort per row block) timed on this host: on
+    every CPU of the process's affinity mask (a forked process pool over row
+    blocks) and on one core, for the large batch; the pool also on the decode
+    and tie-heavy batches and on the whole prefill merge (pack + select of
+    T = 8192 rows).  Must run before anything touches the GPU."""
+    import multiprocessing
+
+    from oracle import stable_topk as oracle
+    from stable_top_selection_amd import workloads as W
+
+    cores = len(os.sched_getaffinity(0))
+    out = {"cores_in_affinity_mask": cores}
+    g = W.large()
+    ctx = multiprocessing.get_context("fork")
+    res = {}  # the pool forks at creation: one pool per batch, created after its arrays are set
+    for name, gb, secs in (("large", g, seconds), ("decode_rows16", W.decode(16), min(2.0, seconds)),
+                           ("tie_heavy", W.tie_heavy(), min(2.0, seconds))):
+        _CPU.update(scores=gb.scores, ids=gb.ids, k=gb.k)
+        with ctx.Pool(cores) as pool:
+            blocks = _blocks(gb.rows, cores)
+            pool.map(_cpu_select_rows, blocks, chunksize=1)  # warm the workers
+            times = _timed_runs(lambda: pool.map(_cpu_select_rows, blocks, chunksize=1), secs)
+        t = statistics.median(times)
+        res[name] = {"candidates_per_s": gb.rows * gb.num_cand / t, "ms_per_batch": round(1e3 * t, 3),
+                     "runs": len(times), "batch": f"{gb.rows} x {gb.num_cand}, K {gb.k}"}
+        log(f"[cpu oracle, {cores} cores] {name}: {t * 1e3:.1f} ms per batch")
+    times = _timed_runs(lambda: oracle.select(g.scores, g.ids, g.k), min(3.0, seconds))
+    t1 = statistics.median(times)
+    res["large_one_core"] = {"candidates_per_s": g.rows * g.num_cand / t1, "ms_per_batch": round(1e3 * t1, 3),
+                             "runs": len(times), "cores": 1}
+    log(f"[cpu oracle, 1 core] large: {t1 * 1e3:.1f} ms per batch")
+    sh = W.prefill()
+    _CPU.update(shards=sh)
+    with ctx.Pool(cores) as pool:
+        blocks = _blocks(sh.rows, 4 * cores)
+        times = _timed_runs(lambda: pool.map(_cpu_merge_rows, blocks, chunksize=1), 0.0, min_runs=2)
+    tm = statistics.median(times)
+    res["prefill_merge_T8192"] = {"candidates_per_s": sh.rows * sh.dcp * sh.local_k / tm, "ms": round(1e3 * tm, 1),
+                                  "runs": len(times),
+                                  "work": f"pack + select of T={sh.rows} rows, DCP {sh.dcp} x local K {sh.local_k}, "
+                                          f"K {sh.k}"}
+    log(f"[cpu oracle, {cores} cores] prefill merge T={sh.rows}: {tm * 1e3:.0f} ms")
+    _CPU.clear()
+    big = res["large"]
+    head = {"value": big["candidates_per_s"], "unit": "candidates/s", "cores": cores, "kind": "oracle",
             "sample": f"the full {g.name} batch ({g.rows} x {g.num_cand}, K {g.k}) through the numpy oracle, "
-                      f"{len(times)} runs in {sum(times):.1f} s, median {t * 1e3:.1f} ms per batch",
-            "host_cpus_visible": len(os.sched_getaffinity(0))}
+                      f"rows split over a pool of {cores} forked processes, median of {big['runs']} runs "
+                      f"({big['ms_per_batch']:.1f} ms per batch)"}
+    out.update(res)
+    return head, out
 
 
 def traffic_record(launch_us):
@@ -475,6 +588,9 @@ def main():
         sys.exit(2)
     from stable_top_selection_amd import workloads as W
 
+    # the CPU oracle first: its process pool forks before this process
+    # touches the GPU
+    cpu, cpu_extra = (None, None) if (args.no_cpu or args.pmc) else cpu_baselines(args.cpu_seconds)
     run = Runner()
     if args.pmc:
         pmc_mode(run)
@@ -537,17 +653,14 @@ def main():
         extra["local_topk"] = bench_local(run, args.steps, args.warmup, args.trials)
         log(f"[local] {extra['local_topk']}")
 
-    cpu = None
-    if not args.no_cpu:
-        cpu = cpu_baseline(g, args.cpu_seconds)
-        log(f"[cpu oracle] {cpu['value']:.3e} candidates/s ({cpu['sample']})")
-        # the same oracle on the decode and tie-heavy batches (about 2 s each)
-        others = {}
-        for name, go in (("decode_rows16", W.decode(16)), ("tie_heavy", W.tie_heavy())):
-            c = cpu_baseline(go, min(2.0, args.cpu_seconds))
-            others[name] = {"candidates_per_s": round(c["value"]), "cores": c["cores"], "sample": c["sample"]}
-            log(f"[cpu oracle] {name}: {c['value']:.3e} candidates/s ({c['sample']})")
-        extra["cpu_oracle_other_batches"] = others
+    if cpu_extra is not None:
+        extra["cpu_oracle"] = cpu_extra
+        gpu_us = {"large": us}
+        if "decode_latency_us" in extra:
+            gpu_us["decode_rows16"] = extra["decode_latency_us"]["rows16"]["cold_us"]
+        if "tie_heavy_latency_us" in extra:
+            gpu_us["tie_heavy"] = extra["tie_heavy_latency_us"]["cold_us"]
+        extra["cpu_oracle"]["gpu_us_same_batches"] = gpu_us
 
     traffic = traffic_record(us)
     line = {
@@ -555,7 +668,7 @@ def main():
         "value": g.rows * g.num_cand / (us * 1e-6),
         "unit": "candidates/s",
         "n_gpus": 1,
-        "steps": args.steps,
+        "steps": res["launches"] * args.trials,
         "warmup": args.warmup,
         "ms_per_step": us * 1e-3,
         "higher_is_better": True,
@@ -567,6 +680,8 @@ def main():
                                "inputs rotated through a 576+ MiB pool (HBM-cold)",
                    "rows": g.rows, "num_cand": g.num_cand, "k": g.k},
         "us_per_launch": us,
+        "timing": {"launches_per_trial": res["launches"], "trials": args.trials, "steps_requested": args.steps,
+                   "stat": "median over trials of the per-launch time of one graph replay"},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": traffic,
                      "kernel": "stable_topk_kernel<512, 2, 16, full, GatheredSource, PairSink>", "algorithmic_bytes_per_launch": per_launch_bytes},

@@ -1240,7 +1240,10 @@ hipError_t launch_sized(const Source& src, const Sink& sink, bool uniform_rows, 
     if (num_cand <= 2048) return launch<256, 4, 8>(src, sink, u, rows, num_cand, k, stream);
     if (num_cand <= 4096) return launch<512, 4, 8>(src, sink, u, rows, num_cand, k, stream);
     if (num_cand <= 8192) return launch<512, 4, 16>(src, sink, u, rows, num_cand, k, stream);
-    return launch<512, 4, 32>(src, sink, u, rows, num_cand, k, stream);
+    // 32 items per thread: two-item loads (any source that allows four-item
+    // loads allows two), because the four-item form of the partial-row kernel
+    // needs more than 256 VGPRs and spills
+    return launch<512, 2, 32>(src, sink, u, rows, num_cand, k, stream);
   } else {
     return launch_sized_narrow<VEC>(src, sink, u, rows, num_cand, k, stream);
   }

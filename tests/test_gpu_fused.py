@@ -131,6 +131,20 @@ def test_fused_narrow_load_paths(local_k, shift):
     _parity(sh, 200, f"misaligned by {4 * shift} B, local_k={local_k}", misalign=shift)
 
 
+@pytest.mark.parametrize("dcp,local_k", [(3, 4096), (5, 2048), (6, 2048), (8, 1536)])
+@pytest.mark.parametrize("misalign", [0, 2, 1])
+@pytest.mark.parametrize("dist", ["normal", "levels"])
+def test_fused_between_8192_and_16384_candidates(dcp, local_k, misalign, dist):
+    """Rows of 8192 < dcp * local_k < 16384 candidates take the partial-row
+    kernels of 32 items per thread (the last positions of every thread's
+    range are masked out).  16-, 8- and 4-byte aligned arrays (the three load
+    widths), 5% invalid slots, smooth and tie-heavy scores."""
+    sh = _random_shards(24, dcp, local_k, seed=dcp * 7919 + local_k + misalign * 31 + (dist == "levels"),
+                        invalid_frac=0.05, dist=dist)
+    _parity(sh, 2048, f"dcp={dcp} local_k={local_k} ({dcp * local_k} candidates) misalign={4 * misalign} B {dist}",
+            misalign=misalign)
+
+
 def test_fused_empty_shard_and_no_candidates():
     """A rank whose slots are all invalid packs to padding; local_k = 0 pads
     every output slot."""

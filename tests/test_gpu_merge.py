@@ -125,3 +125,61 @@ def test_merge_workspace_errors():
     with pytest.raises(B.DcpTopkError) as e:  # 8 bytes past a 256-byte boundary
         B.merge_chunked(sc, ix, rs, offs, 16, workspace=big[8:8 + need])
     assert e.value.status == B.EWORKSPACE
+
+
+def test_merge_chunked_workspace_canaries():
+    """Guard bytes just before the workspace and just past its ``need`` bytes
+    survive the chunked merge (T = 2*1024+5 rows: three chunks, the last one
+    short)."""
+    rows = 2 * 1024 + 5
+    sh = W.prefill(rows=rows, seed=2053)
+    sc, ix, rs, offs = _shards_to_dev(sh)
+    need = B.merge_workspace_bytes(rows, sh.dcp, sh.local_k)
+    guard = 4096
+    ws_all = torch.full((guard + need + guard,), 0xA5, dtype=torch.uint8, device=DEV)
+    ws = ws_all[guard:guard + need]
+    assert ws.data_ptr() % B.WORKSPACE_ALIGN == 0
+    out = B.merge_chunked(sc, ix, rs, offs, sh.k, workspace=ws)
+    torch.cuda.synchronize()
+    g = ws_all.cpu().numpy()
+    assert np.all(g[:guard] == 0xA5), "wrote before the workspace"
+    assert np.all(g[guard + need:] == 0xA5), "wrote past the workspace's required bytes"
+    want_s, want_i = O.merge(sh.scores, sh.local_idx, sh.row_starts, sh.rank_offsets, sh.k)
+    o = out.cpu().numpy()
+    assert np.array_equal(o[..., 0].view(np.uint32), want_s.view(np.uint32)) and np.array_equal(o[..., 1], want_i)
+
+
+def test_merge_chunked_graph_replay_changing_inputs():
+    """The chunked merge (T = 1024+37 rows: two chunks through one workspace)
+    captured once into a HIP graph, then replayed three times with new inputs
+    copied into the captured buffers between replays (PR #47348, Summary: the
+    merge is graph-capturable; PR #50009, Validation: replay with changing
+    inputs).  Every replay matches the oracle on that replay's inputs."""
+    rows = 1024 + 37
+    shards = [W.prefill(rows=rows, seed=700 + i) for i in range(4)]
+    sc, ix, rs, offs = _shards_to_dev(shards[0])
+    need = B.merge_workspace_bytes(rows, 4, 2048)
+    ws = torch.empty(need, dtype=torch.uint8, device=DEV)
+    out = torch.empty((rows, 2048, 2), dtype=torch.int32, device=DEV)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        B.merge_chunked(sc, ix, rs, offs, 2048, workspace=ws, out=out)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        B.merge_chunked(sc, ix, rs, offs, 2048, workspace=ws, out=out)
+    for rep, sh in enumerate(shards[1:] + shards[:1]):
+        for r in range(4):
+            sc[r].copy_(to_dev(sh.scores[r]))
+            ix[r].copy_(to_dev(sh.local_idx[r]))
+            rs[r].copy_(to_dev(sh.row_starts[r]))
+        out.fill_(0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        want_s, want_i = O.merge(sh.scores, sh.local_idx, sh.row_starts, sh.rank_offsets, 2048)
+        o = out.cpu().numpy()
+        assert np.array_equal(o[..., 0].view(np.uint32), want_s.view(np.uint32)), f"replay {rep}: scores"
+        assert np.array_equal(o[..., 1], want_i), f"replay {rep}: ids"

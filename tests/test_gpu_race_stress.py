@@ -78,6 +78,25 @@ def test_fused_merge():
     assert np.array_equal(o[..., 0].view(np.uint32), want_s.view(np.uint32)) and np.array_equal(o[..., 1], want_i)
 
 
+def test_fused_merge_partial_32_item_rows():
+    """DCP 6 x local K 2048 = 12288 candidates: the partial-row 32-item kernel,
+    tie-heavy scores with invalid slots."""
+    rng = np.random.default_rng(6144)
+    dcp, rows, lk, k = 6, 16, 2048, 2048
+    scores = W.TIE_LEVELS[rng.integers(0, 16, size=(dcp, rows, lk))]
+    idx = np.stack([W.distinct_per_row(rng, rows, lk, 4096) for _ in range(dcp)])
+    idx = np.where(rng.random(idx.shape) < 0.05, np.int32(-1), idx).astype(np.int32)
+    starts = rng.integers(0, 131072, size=(dcp, rows), dtype=np.int32)
+    offs = (np.arange(dcp) * 135168).astype(np.int32)
+    print("[race stress] fused merge dcp 6 x 2048, levels", flush=True)
+    out = B.merge_fused([to_dev(scores[r]) for r in range(dcp)], [to_dev(idx[r]) for r in range(dcp)],
+                        [to_dev(starts[r]) for r in range(dcp)], [int(x) for x in offs], k)
+    torch.cuda.synchronize()
+    o = out.cpu().numpy()
+    want_s, want_i = O.merge(scores, idx, starts, offs, k)
+    assert np.array_equal(o[..., 0].view(np.uint32), want_s.view(np.uint32)) and np.array_equal(o[..., 1], want_i)
+
+
 def test_local_topk():
     d = W.local(rows=64, dist="levels", with_lengths=True)
     print(f"[race stress] local top-K {d.name}", flush=True)
