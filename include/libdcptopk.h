@@ -29,7 +29,9 @@
  *    call only.  The library allocates nothing, keeps no pointer and no global
  *    state, and synchronises nothing: every call only enqueues work on
  *    `stream`, so calls are safe from several host threads on several streams
- *    and can be captured into a HIP graph.
+ *    and can be captured into a HIP graph.  The one exception is
+ *    dcp_topk_merge_chunked_static, whose workspace is a static buffer of the
+ *    library on each GPU (see there).
  *  - Errors are returned as negative status codes and never abort.  Arguments
  *    are checked before anything is enqueued; a failed check enqueues nothing.
  *    Faults inside a kernel surface at the caller's next synchronisation, as
@@ -79,7 +81,10 @@ enum {
                                  one entry point); the caller can fall back to
                                  another selector */
   DCP_TOPK_EWORKSPACE = -3,   /* workspace too small or not 256-byte aligned */
-  DCP_TOPK_EHIP = -4          /* the HIP runtime rejected a launch */
+  DCP_TOPK_EHIP = -4,         /* the HIP runtime rejected a launch */
+  DCP_TOPK_ESCRATCH = -5      /* the shape needs more scratch than
+                                 dcp_topk_merge_chunked_static's static
+                                 buffer (DCP_TOPK_STATIC_SCRATCH_BYTES) */
 };
 
 /*
@@ -230,6 +235,36 @@ DCP_TOPK_API int dcp_topk_merge_fused(const float* const* local_scores, const in
 DCP_TOPK_API int dcp_topk_local(const float* scores, int64_t score_row_stride, const int32_t* lengths,
                    int32_t rows, int32_t num_cols, int32_t k, float* out_scores, int32_t* out_idx,
                    int64_t out_row_stride, hipStream_t stream);
+
+/* Bytes of the static device buffer dcp_topk_merge_chunked_static uses on
+ * each GPU: one DCP_TOPK_MERGE_ROWS-row chunk of 8192 candidates (DCP 4 x
+ * local K 2048), 64 MiB. */
+#define DCP_TOPK_STATIC_SCRATCH_BYTES (64u << 20)
+
+/*
+ * dcp_topk_merge_chunked_static — dcp_topk_merge_chunked for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc): the same merge, bit for bit, with
+ * its chunk workspace in a static device buffer of the library instead of a
+ * caller workspace.  It calls no hipMalloc, hipFree or other allocating
+ * routine.
+ *
+ *   arguments     as in dcp_topk_merge_chunked, without workspace and
+ *                 workspace_bytes; `stream` must belong to the current device
+ *
+ * The buffer holds DCP_TOPK_STATIC_SCRATCH_BYTES bytes on every GPU the
+ * library runs on, from the first call on that GPU until the process ends.
+ * Shapes whose dcp_topk_merge_workspace_bytes(rows, dcp, local_k) exceeds it
+ * return DCP_TOPK_ESCRATCH and enqueue nothing (with 1024 or more rows: dcp *
+ * local_k > 8192).  Every call on one GPU uses that GPU's one buffer:
+ * calls that overlap in time on one GPU (on different streams, or from
+ * several host threads without ordering) race and give undefined results;
+ * calls on one stream are ordered and safe.  The buffer needs no clearing
+ * (every chunk's pack writes all of it before the select reads it).
+ */
+DCP_TOPK_API int dcp_topk_merge_chunked_static(const float* const* local_scores, const int32_t* const* local_idx,
+                           const int32_t* const* row_starts, const int32_t* rank_offsets, int32_t dcp,
+                           int32_t rows, int32_t local_k, int32_t k, dcp_topk_cand* out, hipStream_t stream);
 
 /* Static, human-readable name of a status code. */
 DCP_TOPK_API const char* dcp_topk_status_string(int status);

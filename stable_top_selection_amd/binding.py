@@ -19,11 +19,12 @@ import torch
 
 from .build import INCLUDE, LIB_PATH
 
-OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP = 0, -1, -2, -3, -4
+OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP, ESCRATCH = 0, -1, -2, -3, -4, -5
 MERGE_ROWS = 1024
 MAX_CANDIDATES = 16384
 FUSED_MAX_RANKS = 16
 WORKSPACE_ALIGN = 256
+STATIC_SCRATCH_BYTES = 64 << 20
 
 _lib = None
 
@@ -62,6 +63,8 @@ def open_library(path: str) -> ctypes.CDLL:
     lib.dcp_topk_merge_workspace_bytes.restype = sz
     lib.dcp_topk_merge_chunked.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, vp, sz, vp, vp]
     lib.dcp_topk_merge_chunked.restype = ctypes.c_int
+    lib.dcp_topk_merge_chunked_static.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, vp, vp]
+    lib.dcp_topk_merge_chunked_static.restype = ctypes.c_int
     lib.dcp_topk_merge_fused.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, vp, vp]
     lib.dcp_topk_merge_fused.restype = ctypes.c_int
     lib.dcp_topk_local.argtypes = [vp, i64, vp, i32, i32, i32, vp, vp, i64, vp]
@@ -189,6 +192,27 @@ def merge_chunked(local_scores: Sequence[torch.Tensor], local_idx: Sequence[torc
     _check("dcp_topk_merge_chunked",
            lib.dcp_topk_merge_chunked(sp, ip, rp, offs, dcp, rows, local_k, int(k), _p(workspace.data_ptr()),
                                       workspace.numel(), _p(out.data_ptr()), _stream(device)))
+    return out
+
+
+def merge_chunked_static(local_scores: Sequence[torch.Tensor], local_idx: Sequence[torch.Tensor],
+                         row_starts: Sequence[torch.Tensor], rank_offsets: Sequence[int], k: int,
+                         out: torch.Tensor | None = None) -> torch.Tensor:
+    """The chunked merge with the library's static per-GPU workspace (no
+    allocation in the library): same result as merge_chunked.  Calls that
+    overlap in time on one GPU race."""
+    lib = load_library()
+    dcp = len(local_scores)
+    rows, local_k = _check_ranks(local_scores, local_idx, row_starts)
+    device = local_scores[0].device
+    if out is None:
+        out = torch.empty((rows, k, 2), dtype=torch.int32, device=device)
+    _require(out, "out", torch.int32, 3)
+    arrays = _RankArrays(local_scores, local_idx, row_starts, rank_offsets)  # alive for the call
+    sp, ip, rp, offs = arrays.args()
+    _check("dcp_topk_merge_chunked_static",
+           lib.dcp_topk_merge_chunked_static(sp, ip, rp, offs, dcp, rows, local_k, int(k), _p(out.data_ptr()),
+                                             _stream(device)))
     return out
 
 

@@ -95,6 +95,63 @@ int check_ranks(const float* const* local_scores, const int32_t* const* local_id
 
 }  // namespace
 
+namespace dcptopk {
+
+int check_merge_shape(const float* const* local_scores, const int32_t* const* local_idx,
+                      const int32_t* const* row_starts, const int32_t* rank_offsets, int32_t dcp, int32_t rows,
+                      int32_t local_k, int32_t k, bool* nothing_to_do) {
+  *nothing_to_do = false;
+  if (dcp < 1 || rows < 0 || local_k < 0 || k < 1) return DCP_TOPK_EINVAL;
+  if (local_scores == nullptr || local_idx == nullptr || row_starts == nullptr || rank_offsets == nullptr)
+    return DCP_TOPK_EINVAL;
+  if (static_cast<int64_t>(dcp) * local_k > DCP_TOPK_MAX_CANDIDATES || k > DCP_TOPK_MAX_CANDIDATES)
+    return DCP_TOPK_EUNSUPPORTED;
+  *nothing_to_do = rows == 0;
+  return DCP_TOPK_OK;
+}
+
+int merge_chunks(const float* const* local_scores, const int32_t* const* local_idx, const int32_t* const* row_starts,
+                 const int32_t* rank_offsets, int32_t dcp, int32_t rows, int32_t local_k, int32_t k, void* workspace,
+                 dcp_topk_cand* out, hipStream_t stream) {
+  const int32_t num_cand = dcp * local_k;
+  const size_t need = dcp_topk_merge_workspace_bytes(rows, dcp, local_k);
+  if (out == nullptr || !aligned(out, kCandBytes)) return DCP_TOPK_EINVAL;
+  Span ws{reinterpret_cast<uintptr_t>(workspace), need};
+  Span o;
+  if (!strided_span(out, rows, k, k, kCandBytes, &o)) return DCP_TOPK_EINVAL;
+  if (overlap(ws, o)) return DCP_TOPK_EINVAL;
+  // The workspace holds one chunk (at most DCP_TOPK_MERGE_ROWS rows); the
+  // inputs span all rows.
+  if (local_k > 0) {
+    const Span outputs[2] = {o, ws};
+    const int st = check_ranks(local_scores, local_idx, row_starts, dcp, rows, local_k, outputs, 2);
+    if (st != DCP_TOPK_OK) return st;
+  }
+
+  dcp_topk_cand* buf = static_cast<dcp_topk_cand*>(workspace);
+  for (int64_t c0 = 0; c0 < rows; c0 += DCP_TOPK_MERGE_ROWS) {
+    const int32_t n = static_cast<int32_t>(rows - c0 < DCP_TOPK_MERGE_ROWS ? rows - c0 : DCP_TOPK_MERGE_ROWS);
+    if (local_k > 0) {
+      for (int g = 0; g < dcp; g += kMaxPackRanks) {
+        const int nr = dcp - g < kMaxPackRanks ? dcp - g : kMaxPackRanks;
+        PackRank pr[kMaxPackRanks];
+        for (int r = 0; r < nr; ++r) {
+          pr[r] = {local_scores[g + r] + c0 * local_k, local_idx[g + r] + c0 * local_k, row_starts[g + r] + c0,
+                   rank_offsets[g + r]};
+        }
+        const hipError_t e = launch_pack(pr, nr, local_k, n, local_k, buf + static_cast<int64_t>(g) * local_k,
+                                         num_cand, stream);
+        if (e != hipSuccess) return DCP_TOPK_EHIP;
+      }
+    }
+    const hipError_t e = launch_select(buf, n, num_cand, k, out + c0 * k, stream);
+    if (e != hipSuccess) return DCP_TOPK_EHIP;
+  }
+  return DCP_TOPK_OK;
+}
+
+}  // namespace dcptopk
+
 extern "C" {
 
 const char* dcp_topk_status_string(int status) {
@@ -109,6 +166,8 @@ const char* dcp_topk_status_string(int status) {
       return "workspace too small or misaligned";
     case DCP_TOPK_EHIP:
       return "HIP launch failed";
+    case DCP_TOPK_ESCRATCH:
+      return "shape needs more than the static scratch buffer";
     default:
       return "unknown status";
   }
@@ -140,49 +199,15 @@ int dcp_topk_merge_chunked(const float* const* local_scores, const int32_t* cons
                            const int32_t* const* row_starts, const int32_t* rank_offsets, int32_t dcp, int32_t rows,
                            int32_t local_k, int32_t k, void* workspace, size_t workspace_bytes, dcp_topk_cand* out,
                            hipStream_t stream) {
-  if (dcp < 1 || rows < 0 || local_k < 0 || k < 1) return DCP_TOPK_EINVAL;
-  if (local_scores == nullptr || local_idx == nullptr || row_starts == nullptr || rank_offsets == nullptr)
-    return DCP_TOPK_EINVAL;
-  if (static_cast<int64_t>(dcp) * local_k > DCP_TOPK_MAX_CANDIDATES || k > DCP_TOPK_MAX_CANDIDATES)
-    return DCP_TOPK_EUNSUPPORTED;
-  if (rows == 0) return DCP_TOPK_OK;
-  const int32_t num_cand = dcp * local_k;
+  bool nothing = false;
+  int st = dcptopk::check_merge_shape(local_scores, local_idx, row_starts, rank_offsets, dcp, rows, local_k, k,
+                                      &nothing);
+  if (st != DCP_TOPK_OK || nothing) return st;
   const size_t need = dcp_topk_merge_workspace_bytes(rows, dcp, local_k);
   if (need > 0 && (workspace == nullptr || !aligned(workspace, DCP_TOPK_WORKSPACE_ALIGN))) return DCP_TOPK_EWORKSPACE;
   if (workspace_bytes < need) return DCP_TOPK_EWORKSPACE;
-  if (out == nullptr || !aligned(out, kCandBytes)) return DCP_TOPK_EINVAL;
-  Span ws{reinterpret_cast<uintptr_t>(workspace), need};
-  Span o;
-  if (!strided_span(out, rows, k, k, kCandBytes, &o)) return DCP_TOPK_EINVAL;
-  if (overlap(ws, o)) return DCP_TOPK_EINVAL;
-  // The workspace holds one chunk (at most DCP_TOPK_MERGE_ROWS rows); the
-  // inputs span all rows.
-  if (local_k > 0) {
-    const Span outputs[2] = {o, ws};
-    const int st = check_ranks(local_scores, local_idx, row_starts, dcp, rows, local_k, outputs, 2);
-    if (st != DCP_TOPK_OK) return st;
-  }
-
-  dcp_topk_cand* buf = static_cast<dcp_topk_cand*>(workspace);
-  for (int64_t c0 = 0; c0 < rows; c0 += DCP_TOPK_MERGE_ROWS) {
-    const int32_t n = static_cast<int32_t>(rows - c0 < DCP_TOPK_MERGE_ROWS ? rows - c0 : DCP_TOPK_MERGE_ROWS);
-    if (local_k > 0) {
-      for (int g = 0; g < dcp; g += dcptopk::kMaxPackRanks) {
-        const int nr = dcp - g < dcptopk::kMaxPackRanks ? dcp - g : dcptopk::kMaxPackRanks;
-        dcptopk::PackRank pr[dcptopk::kMaxPackRanks];
-        for (int r = 0; r < nr; ++r) {
-          pr[r] = {local_scores[g + r] + c0 * local_k, local_idx[g + r] + c0 * local_k, row_starts[g + r] + c0,
-                   rank_offsets[g + r]};
-        }
-        const hipError_t e = dcptopk::launch_pack(pr, nr, local_k, n, local_k, buf + static_cast<int64_t>(g) * local_k,
-                                                  num_cand, stream);
-        if (e != hipSuccess) return DCP_TOPK_EHIP;
-      }
-    }
-    const hipError_t e = dcptopk::launch_select(buf, n, num_cand, k, out + c0 * k, stream);
-    if (e != hipSuccess) return DCP_TOPK_EHIP;
-  }
-  return DCP_TOPK_OK;
+  return dcptopk::merge_chunks(local_scores, local_idx, row_starts, rank_offsets, dcp, rows, local_k, k, workspace,
+                               out, stream);
 }
 
 int dcp_topk_merge_fused(const float* const* local_scores, const int32_t* const* local_idx,

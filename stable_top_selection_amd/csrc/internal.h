@@ -53,4 +53,20 @@ hipError_t launch_local(const float* scores, int64_t score_row_stride, const int
 hipError_t launch_pack(const PackRank* ranks, int nranks, int64_t src_row_stride, int32_t rows,
                        int32_t local_k, dcp_topk_cand* dst, int64_t dst_row_stride, hipStream_t stream);
 
+// Checks of a chunked merge's shape and host arrays (every check of
+// dcp_topk_merge_chunked that does not involve the workspace or the output).
+// *nothing_to_do is set when rows == 0.
+int check_merge_shape(const float* const* local_scores, const int32_t* const* local_idx,
+                      const int32_t* const* row_starts, const int32_t* rank_offsets, int32_t dcp, int32_t rows,
+                      int32_t local_k, int32_t k, bool* nothing_to_do);
+
+// The rest of the chunked merge once its shape and workspace are valid: the
+// output and rank-array checks (nothing may overlap the workspace's
+// dcp_topk_merge_workspace_bytes(rows, dcp, local_k) bytes or the output),
+// then, per DCP_TOPK_MERGE_ROWS-row chunk, the pack of every rank into the
+// workspace and the select of the chunk into `out`.  Returns a status code.
+int merge_chunks(const float* const* local_scores, const int32_t* const* local_idx, const int32_t* const* row_starts,
+                 const int32_t* rank_offsets, int32_t dcp, int32_t rows, int32_t local_k, int32_t k, void* workspace,
+                 dcp_topk_cand* out, hipStream_t stream);
+
 }  // namespace dcptopk

@@ -39,6 +39,10 @@ int main(void) {
            dcp_topk_merge_chunked(sc, ix, rs, offs, 1, 4, 128, 10, (void*)(uintptr_t)0x7F0050000000ull, 16, fake_out,
                                   NULL),
            DCP_TOPK_EWORKSPACE);
+    expect("static-scratch merge, 1024 rows of dcp 1 x 16384 (128 MiB of workspace)",
+           dcp_topk_merge_chunked_static(sc, ix, rs, offs, 1, 1024, 16384, 10, fake_out, NULL), DCP_TOPK_ESCRATCH);
+    expect("static-scratch merge, no rows", dcp_topk_merge_chunked_static(sc, ix, rs, offs, 1, 0, 2048, 10, NULL, NULL),
+           DCP_TOPK_OK);
   }
   expect("local top-K, no rows", dcp_topk_local(NULL, 0, NULL, 0, 4096, 2048, NULL, NULL, 2048, NULL), DCP_TOPK_OK);
   expect("local top-K, k = 0",

@@ -24,8 +24,8 @@ def lib():
 def test_exports_every_header_function(lib):
     names = B.header_functions()
     assert set(names) == {"dcp_topk_pack", "dcp_topk_select", "dcp_topk_merge_workspace_bytes",
-                          "dcp_topk_merge_chunked", "dcp_topk_merge_fused", "dcp_topk_local",
-                          "dcp_topk_status_string"}
+                          "dcp_topk_merge_chunked", "dcp_topk_merge_chunked_static", "dcp_topk_merge_fused",
+                          "dcp_topk_local", "dcp_topk_status_string"}
     for n in names:
         assert hasattr(lib, n), n
     exported = subprocess.run(["nm", "-D", "--defined-only", LIB_PATH], capture_output=True, text=True).stdout
@@ -51,6 +51,7 @@ def test_status_strings(lib):
     assert "unsupported" in B.status_string(-2)
     assert "workspace" in B.status_string(-3)
     assert "HIP" in B.status_string(-4)
+    assert "static scratch" in B.status_string(-5)
     assert B.status_string(99) == "unknown status"
 
 
