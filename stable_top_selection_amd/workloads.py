@@ -306,4 +306,38 @@ def random_gathered(rows: int, num_cand: int, k: int, seed: int, dist: str = "no
                     np.ascontiguousarray(ids), k=k)
 
 
+def block_heads(rows: int, seed: int, heads_high: bool, num_cand: int = 8192, k: int = 2048) -> Gathered:
+    """Rows whose first 256 candidates of every 1024-candidate block come from
+    another distribution than the rest: N(0,1) heads and N(6,1) tails, or the
+    reverse (``heads_high``).  Ids distinct per row."""
+    rng = np.random.default_rng(seed)
+    head = (np.arange(num_cand) % 1024) < 256
+    lo = rng.standard_normal((rows, num_cand), dtype=np.float32)
+    hi = (rng.standard_normal((rows, num_cand), dtype=np.float32) + np.float32(6.0)).astype(np.float32)
+    scores = np.where(head, hi, lo) if heads_high else np.where(head, lo, hi)
+    ids = distinct_per_row(rng, rows, num_cand, 4 * num_cand)
+    return Gathered(f"block_heads_{'high' if heads_high else 'low'}_{rows}x{num_cand}_k{k}",
+                    np.ascontiguousarray(scores.astype(np.float32)), ids, k=k)
+
+
+def crowded(rows: int, seed: int, tie: bool, num_cand: int = 8192, k: int = 2048) -> Gathered:
+    """Rows with a crowd of 64 near-equal scores (5.45 + 1e-6 N(0,1), or
+    exactly 5.45 with ``tie``) inside 1000 scores U(5.0, 5.9), above them 1500
+    scores U(10, 20), below them the rest U(-20, -10); positions shuffled.
+    With k = 2048 the k-th best score falls among the crowd."""
+    rng = np.random.default_rng(seed)
+    n_top, n_mid, n_crowd = 1500, 1000, 64
+    n_low = num_cand - n_top - n_mid - n_crowd
+    scores = np.empty((rows, num_cand), dtype=np.float32)
+    for r in range(rows):
+        crowd = np.full(n_crowd, 5.45, dtype=np.float32) if tie else \
+            (np.float32(5.45) + np.float32(1e-6) * rng.standard_normal(n_crowd, dtype=np.float32)).astype(np.float32)
+        parts = [rng.uniform(10.0, 20.0, n_top), rng.uniform(5.0, 5.9, n_mid), crowd,
+                 rng.uniform(-20.0, -10.0, n_low)]
+        row = np.concatenate([x.astype(np.float32) for x in parts])
+        scores[r] = row[rng.permutation(num_cand)]
+    ids = distinct_per_row(rng, rows, num_cand, 4 * num_cand)
+    return Gathered(f"crowded_{'tie' if tie else 'distinct'}_{rows}x{num_cand}_k{k}", scores, ids, k=k)
+
+
 CONFIG_NAMES = ("tiny", "decode", "large", "tie_heavy", "prefill")

@@ -65,6 +65,16 @@ def test_ragged_and_degenerate(rows, c, k, dist, kw):
     _select(W.random_gathered(rows, c, k, seed=900 + c + k, dist=dist, **kw), f"{dist} {kw}")
 
 
+@pytest.mark.parametrize("make", [lambda: W.block_heads(32, 601, heads_high=False),
+                                  lambda: W.block_heads(32, 602, heads_high=True),
+                                  lambda: W.crowded(32, 603, tie=False), lambda: W.crowded(32, 604, tie=True)],
+                         ids=["block_heads_low", "block_heads_high", "crowded_sub_bin", "crowded_tie"])
+def test_adversarial_rows(make):
+    """Rows whose first chunks are unlike the rest, a crowded threshold sub-bin
+    (list passes past the first) and a crowded tie (id passes)."""
+    _select(make(), "adversarial rows")
+
+
 def test_fused_merge():
     sh = W.fused()
     print(f"[race stress] fused merge {sh.name}", flush=True)
