@@ -401,7 +401,9 @@ def bench_fused(run, steps, warmup, trials):
 
 def bench_local(run, steps, warmup, trials):
     """Local top-K, 2048 of 4096 columns per row: rows 64 (the largest decode
-    row count measured on PR #50009) and 256, HBM-cold pools, and rows 64 warm."""
+    row count measured on PR #50009) and 256, HBM-cold pools, rows 64 warm,
+    and with per-row lengths (rows 64 and 256; 2048 rows of 8192 columns,
+    8 rows per CU, where the partial-row kernels' occupancy shows)."""
     import numpy as np
 
     from oracle import stable_topk as oracle
@@ -409,9 +411,9 @@ def bench_local(run, steps, warmup, trials):
 
     torch = run.torch
     res = {}
-    for rows, cold, lengths in ((64, True, False), (64, False, False), (256, True, False), (64, True, True),
-                                (256, True, True)):
-        d = W.local(rows=rows, with_lengths=lengths)
+    for rows, cold, lengths, ncols in ((64, True, False, 4096), (64, False, False, 4096), (256, True, False, 4096),
+                                       (64, True, True, 4096), (256, True, True, 4096), (2048, True, True, 8192)):
+        d = W.local(rows=rows, num_cols=ncols, with_lengths=lengths)
         cols, k = d.num_cols, d.k
         per = rows * cols * 4 + rows * k * 8
         n = max(1, -(-COLD_POOL_BYTES // per)) if cold else 1
@@ -439,13 +441,14 @@ def bench_local(run, steps, warmup, trials):
             if not (np.array_equal(os_[i].cpu().numpy().view(np.uint32), ws.view(np.uint32))
                     and np.array_equal(oi[i].cpu().numpy(), wi)):
                 raise AssertionError(f"local top-K output differs from the oracle ({d.name})")
-        res[f"rows{rows}_{'cold' if cold else 'warm'}{'_lengths' if lengths else ''}"] = {
+        res[f"rows{rows}{'' if ncols == 4096 else f'_cols{ncols}'}_{'cold' if cold else 'warm'}"
+            f"{'_lengths' if lengths else ''}"] = {
             "us_per_launch": round(us, 3), "GBps": round(per / (us * 1e-6) / 1e9, 1), "pool_buffers": n,
             "algorithmic_bytes_per_launch": per}
         del graph, src, os_, oi, lens
         torch.cuda.empty_cache()
-    res["workload"] = ("local top-K: 4096 fp32 columns per row, k 2048, scores N(0,1); '_lengths' lines take "
-                       "per-row lengths U[0, 4096] (the partial-row kernels)")
+    res["workload"] = ("local top-K: 4096 fp32 columns per row (8192 where named), k 2048, scores N(0,1); "
+                       "'_lengths' lines take per-row lengths U[0, columns] (the partial-row kernels)")
     return res
 
 

@@ -696,8 +696,9 @@ struct RankSource {
       rp[v] = pr.row_starts;
       off[v] = static_cast<uint32_t>(pr.rank_offset);
     }
+    // (wave-uniform: scalar registers)
 #pragma unroll
-    for (int v = 0; v < NV; ++v) aux[v] = static_cast<uint32_t>(rp[v][row]) + off[v];
+    for (int v = 0; v < NV; ++v) aux[v] = uniform(static_cast<uint32_t>(rp[v][row]) + off[v]);
 #pragma unroll
     for (int v = 0; v < NV; ++v) {
       const int64_t at = row * local_k + j0[v] + lane_off;
@@ -911,15 +912,20 @@ __global__ __launch_bounds__(BLOCK) void stable_topk_kernel(Source src, Sink sin
   lds_barrier();
   __builtin_amdgcn_sched_barrier(0);
 
-  // FULL: the row fills every slot (C == BLOCK*N); else the last are masked out
-  uint32_t valid = 0xFFFFFFFFu >> (32 - N);
-  if constexpr (!FULL) {
-    valid = 0;
+  // FULL: the row fills every slot (C == BLOCK*N); else the last are masked
+  // out: item i is valid if its position, first + (i / VEC) * kChunk + i % VEC,
+  // is below C, i.e. if i's offset is below C - first (a compare per use
+  // instead of a mask held in a register)
+  const int room = C - first;  // items of this thread are valid below this offset
+  auto ok = [&](int i) -> bool {
+    return FULL || (i / VEC) * kChunk + i % VEC < room;
+  };
+  auto valid_mask = [&]() -> uint32_t {
+    uint32_t m = 0u;
 #pragma unroll
-    for (int v = 0; v < NV; ++v)
-#pragma unroll
-      for (int j = 0; j < VEC; ++j) valid |= (first + v * kChunk + j < C) ? 1u << (v * VEC + j) : 0u;
-  }
+    for (int i = 0; i < N; ++i) m |= ok(i) ? 1u << i : 0u;
+    return m;
+  };
 
   // 2. pass 0: histogram of the top 11 bits; each item keeps its rank in its
   // bin.  Padding keys (-inf: empty shard slots, which can fill whole ranks)
@@ -947,7 +953,7 @@ __global__ __launch_bounds__(BLOCK) void stable_topk_kernel(Source src, Sink sin
     if (i % VEC == 0) src.template finish<VEC>(i / VEC, aux, bits, idv);
     key[i] = score_key(bits[i]);
     uint32_t* target = key[i] == kPadKey ? pad_word : lds.hist[0] + (key[i] >> 21);
-    if constexpr (!FULL) target = (valid >> i) & 1u ? target : spare;
+    if constexpr (!FULL) target = ok(i) ? target : spare;
     rank_in_bin[i] = lds_add(target);
   }
   lds_barrier();
@@ -974,7 +980,7 @@ __global__ __launch_bounds__(BLOCK) void stable_topk_kernel(Source src, Sink sin
     if (d0 != kPadBin) {
 #pragma unroll
       for (int i = 0; i < N; ++i) {
-        const bool in_bin = ((valid >> i) & 1u) && (key[i] >> 21) == d0;
+        const bool in_bin = ok(i) && (key[i] >> 21) == d0;
         lds.list[in_bin ? rank_in_bin[i] : static_cast<uint32_t>(kListCap)] = make_uint2(key[i], idv[i]);
       }
     } else {
@@ -985,7 +991,7 @@ __global__ __launch_bounds__(BLOCK) void stable_topk_kernel(Source src, Sink sin
       for (int j = 0; j < kPadWords; ++j) pad_base += j < lane % kPadWords ? lds.padcnt[j] : 0u;
 #pragma unroll
       for (int i = 0; i < N; ++i) {
-        const bool in_bin = ((valid >> i) & 1u) && (key[i] >> 21) == d0;
+        const bool in_bin = ok(i) && (key[i] >> 21) == d0;
         const uint32_t slot = rank_in_bin[i] + (key[i] == kPadKey ? pad_base : 0u);
         lds.list[in_bin ? slot : static_cast<uint32_t>(kListCap)] = make_uint2(key[i], idv[i]);
       }
@@ -1077,7 +1083,7 @@ __global__ __launch_bounds__(BLOCK) void stable_topk_kernel(Source src, Sink sin
     uint32_t a = 0u, b = ~0u, c = 0u, e = ~0u;
 #pragma unroll
     for (int i = 0; i < N; ++i) {
-      const bool in_bin = ((valid >> i) & 1u) && (key[i] >> 21) == d0;
+      const bool in_bin = ok(i) && (key[i] >> 21) == d0;
       a |= in_bin ? key[i] : 0u;
       b &= in_bin ? key[i] : ~0u;
       c |= in_bin ? ~idv[i] : 0u;
@@ -1093,9 +1099,9 @@ __global__ __launch_bounds__(BLOCK) void stable_topk_kernel(Source src, Sink sin
       sk.mask = ~0u;
     } else {
       do {
-        radix_pass<BLOCK, 10, 11, false>(lds, p++, key, valid, sk, t, lane);
+        radix_pass<BLOCK, 10, 11, false>(lds, p++, key, valid_mask(), sk, t, lane);
         if (sk.count == sk.need) break;
-        radix_pass<BLOCK, 0, 10, false>(lds, p++, key, valid, sk, t, lane);
+        radix_pass<BLOCK, 0, 10, false>(lds, p++, key, valid_mask(), sk, t, lane);
       } while (false);
     }
     tie = sk.count > sk.need;
@@ -1111,7 +1117,7 @@ __global__ __launch_bounds__(BLOCK) void stable_topk_kernel(Source src, Sink sin
       } else {
         uint32_t tied = 0;
 #pragma unroll
-        for (int i = 0; i < N; ++i) tied |= (((valid >> i) & 1u) && key[i] == sk.prefix) ? (1u << i) : 0u;
+        for (int i = 0; i < N; ++i) tied |= (ok(i) && key[i] == sk.prefix) ? (1u << i) : 0u;
         const int hb = 31 - __builtin_clz(differ);
         if (hb < 31) {
           ik.mask = ~0u << (hb + 1);
@@ -1137,7 +1143,7 @@ __global__ __launch_bounds__(BLOCK) void stable_topk_kernel(Source src, Sink sin
   if (dup) {
     uint32_t same[N];
 #pragma unroll
-    for (int i = 0; i < N; ++i) same[i] = ((valid >> i) & 1u) & (key[i] == sk.prefix) & (~idv[i] == ik.prefix);
+    for (int i = 0; i < N; ++i) same[i] = (ok(i) && key[i] == sk.prefix && ~idv[i] == ik.prefix) ? 1u : 0u;
     position_rank<BLOCK, VEC, N>(same, lds.segment[0], duprank, lane, w);
   }
   uint32_t sel[N];
@@ -1145,21 +1151,21 @@ __global__ __launch_bounds__(BLOCK) void stable_topk_kernel(Source src, Sink sin
     // common case: sk.mask covers the top bits and sk.prefix is zero below
     // them, so (key & mask) >= prefix is simply key >= prefix
 #pragma unroll
-    for (int i = 0; i < N; ++i) sel[i] = (key[i] >= sk.prefix) & ((valid >> i) & 1u);
+    for (int i = 0; i < N; ++i) sel[i] = (ok(i) && key[i] >= sk.prefix) ? 1u : 0u;
   } else if (!dup) {
     // the tied items (key == threshold) are taken by complemented id; the id
     // passes leave ik.prefix zero below ik.mask, so u >= prefix is the test
 #pragma unroll
     for (int i = 0; i < N; ++i) {
       const uint32_t u = ~idv[i];
-      sel[i] = (key[i] > sk.prefix || (key[i] == sk.prefix && u >= ik.prefix)) & ((valid >> i) & 1u);
+      sel[i] = (ok(i) && (key[i] > sk.prefix || (key[i] == sk.prefix && u >= ik.prefix))) ? 1u : 0u;
     }
   } else {
 #pragma unroll
     for (int i = 0; i < N; ++i) {
       const uint32_t u = ~idv[i];
       const bool wins = u > ik.prefix || (u == ik.prefix && duprank[i] < ik.need);
-      sel[i] = (key[i] > sk.prefix || (key[i] == sk.prefix && wins)) & ((valid >> i) & 1u);
+      sel[i] = (ok(i) && (key[i] > sk.prefix || (key[i] == sk.prefix && wins))) ? 1u : 0u;
     }
   }
 

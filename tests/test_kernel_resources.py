@@ -3,11 +3,11 @@ compiler's resource-usage remarks that every build records next to the
 library.
 
 The many-row launches (the fused merge over a prefill batch, the chunked
-merge, the local top-K over many rows) rely on two 512-thread workgroups
-sharing a CU, so that one row's selection overlaps the next row's loads: the
-kernels they use must stay within 128 VGPRs (4 waves per SIMD).  Losing that
-halves their throughput with no change in results, which no parity test
-would notice.
+merge, the local top-K over many rows, with or without per-row lengths) rely
+on two 512-thread workgroups sharing a CU, so that one row's selection
+overlaps the next row's loads: the kernels they use must stay within 128
+VGPRs (4 waves per SIMD).  Losing that halves their throughput with no change
+in results, which no parity test would notice.
 """
 import os
 import re
@@ -20,12 +20,6 @@ pytestmark = pytest.mark.skipif(not os.path.exists(BLD.RESOURCES_PATH),
                                 reason="library not built (run __graft_entry__.build())")
 
 SELECT = re.compile(r"stable_topk_kernelILi(\d+)ELi(\d+)ELi(\d+)ELb([01])ENS0_\d+(\w+?Source)")
-
-# (source, items per load) of the 512-thread, 16-item full-row kernels that
-# launches with 16-byte-aligned arrays take: the gathered select, the fused
-# merge and the local top-K
-MANY_ROW_KERNELS = {("GatheredSource", 2), ("RankSource", 4), ("DenseSource", 4)}
-
 
 def _select_kernels():
     out = []
@@ -43,14 +37,20 @@ def test_every_kernel_reported():
     assert len(_select_kernels()) >= 90
 
 
-def test_many_row_kernels_fit_two_workgroups_per_cu():
+def test_every_8_and_16_item_kernel_fits_two_workgroups_per_cu():
+    """Every 512-thread kernel of 8 or 16 items per thread, full-row or
+    partial-row (per-row lengths, candidate counts that are not a multiple of
+    the block), of every source: at most 128 VGPRs (4 waves per SIMD) and
+    LDS for two workgroups per CU."""
     seen = set()
     for name, block, vec, n, full, source, r in _select_kernels():
-        if block == 512 and full and (n == 8 or (n == 16 and (source, vec) in MANY_ROW_KERNELS)):
-            seen.add((source, vec, n))
+        if block == 512 and n in (8, 16):
+            seen.add((source, vec, n, full))
             assert r["waves_per_simd"] >= 4, f"{name}: {r['vgprs']} VGPRs, {r['waves_per_simd']} waves per SIMD"
             assert 2 * r["lds_bytes"] <= 160 * 1024, f"{name}: {r['lds_bytes']} B of LDS per workgroup"
-    assert {(s, v, 16) for s, v in MANY_ROW_KERNELS} <= seen
+    expected = {(src, vec, n, full) for src in ("GatheredSource", "RankSource", "DenseSource") for vec in (1, 2, 4)
+                for n in (8, 16) for full in (False, True) if not (src == "GatheredSource" and vec == 4)}
+    assert expected <= seen, sorted(expected - seen)
 
 
 def test_no_scratch_in_any_kernel():
