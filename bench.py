@@ -59,8 +59,8 @@ def parse_args():
                    help="select launches per timed trial (at least 200 are timed, a whole number of pool passes)")
     p.add_argument("--warmup", type=int, default=20, help="untimed launches before timing")
     p.add_argument("--trials", type=int, default=7)
-    p.add_argument("--configs", default="large,large_warm,large_eager,decode,tie_heavy,short_context,prefill,fused,local",
-                   help="comma list of large_warm, large_eager, decode, tie_heavy, short_context, prefill, fused, "
+    p.add_argument("--configs", default="large,large_warm,large_eager,decode,split,tie_heavy,short_context,prefill,fused,local",
+                   help="comma list of large_warm, large_eager, decode, split, tie_heavy, short_context, prefill, fused, "
                         "local; the cold large headline always runs (--configs large runs it alone, as profiled)")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU oracle work to time")
@@ -167,8 +167,10 @@ def launches_per_trial(steps, pool):
     return -(-want // pool) * pool
 
 
-def bench_select(run, g, steps, warmup, trials, cold=True):
-    """Median per-launch microseconds of a graph of launches rotating over a cold pool."""
+def bench_select(run, g, steps, warmup, trials, cold=True, select=None):
+    """Median per-launch microseconds of a graph of launches rotating over a
+    cold pool (``select``, with run.select's arguments, replaces the launch)."""
+    select = select or run.select
     inter = g.interleaved()
     pool_bytes = COLD_POOL_BYTES if cold else 0
     ptrs, tensors = make_pool(run, inter, g.k, pool_bytes)
@@ -178,7 +180,7 @@ def bench_select(run, g, steps, warmup, trials, cold=True):
 
     def fn(i):
         cp, op = ptrs[i % n]
-        return lambda sp: run.select(cp, rows, c, k, op, sp)
+        return lambda sp: select(cp, rows, c, k, op, sp)
 
     for i in range(warmup):
         fn(i)(run.stream_ptr())
@@ -194,6 +196,34 @@ def bench_select(run, g, steps, warmup, trials, cold=True):
     return {"us_per_launch": med, "us_trials": [round(x, 4) for x in us], "launches": launches,
             "pool_buffers": n, "outputs_checked": checked, "candidates_per_s": rows * c / (med * 1e-6),
             "GBps": round(gbps, 1), "frac_of_peak": round(gbps / PEAK_HBM_GBS, 4)}
+
+
+def bench_split(run, steps, warmup, trials, decode=None):
+    """The split-row select (each row over 2, 4 or 8 workgroups) on the decode
+    rows, cold, beside the one-workgroup select's cold latency on the same
+    inputs."""
+    from stable_top_selection_amd import workloads as W
+    torch, lib = run.torch, run.lib
+    out = {}
+    for rows in (1, 8, 16, 32, 64):
+        g = W.decode(rows)
+        line = {"one_workgroup_cold_us": decode[f"rows{rows}"]["cold_us"] if decode else None}
+        for parts in (2, 4, 8):
+            ws = run.B.select_split_workspace(rows, g.num_cand, parts, run.dev)
+
+            def split(cp, r, c, k, op, sp, ws=ws, parts=parts):
+                st = lib.dcp_topk_select_split(run.B._p(cp), r, c, k, parts, run.B._p(ws.data_ptr()), ws.numel(),
+                                               run.B._p(op), sp)
+                if st != 0:
+                    raise run.B.DcpTopkError("dcp_topk_select_split", st)
+
+            res = bench_select(run, g, steps, warmup, trials, cold=True, select=split)
+            line[f"parts{parts}_cold_us"] = round(res["us_per_launch"], 3)
+            del ws
+        out[f"rows{rows}"] = line
+        log(f"[split rows={rows}] {line}")
+    torch.cuda.empty_cache()
+    return out
 
 
 def bench_eager(run, g, steps, trials):
@@ -629,6 +659,9 @@ def main():
                                     "cold_frac_of_peak": cold["frac_of_peak"]}
             log(f"[decode rows={rows}] cold {cold['us_per_launch']:.3f} us, warm {hot['us_per_launch']:.3f} us")
         extra["decode_latency_us"] = sweep
+    if "split" in configs:
+        extra["split_rows_latency_us"] = bench_split(run, args.steps, args.warmup, args.trials,
+                                                     extra.get("decode_latency_us"))
     if "tie_heavy" in configs:
         gt = W.tie_heavy()
         cold = bench_select(run, gt, args.steps, args.warmup, args.trials, cold=True)

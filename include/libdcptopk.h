@@ -142,6 +142,55 @@ DCP_TOPK_API int dcp_topk_pack(const float* local_scores, const int32_t* local_i
 DCP_TOPK_API int dcp_topk_select(const dcp_topk_cand* cand, int32_t rows, int32_t num_cand, int32_t k,
                     dcp_topk_cand* out, hipStream_t stream);
 
+/* Most workgroups dcp_topk_select_split spreads one row over. */
+#define DCP_TOPK_SPLIT_MAX_PARTS 8
+
+/*
+ * dcp_topk_select_split_workspace_bytes — workspace that dcp_topk_select_split
+ * needs for (rows, num_cand, parts): four regions, each rounded up to a
+ * multiple of 256 bytes: rows * 16 bytes of counters, rows * parts * 8224
+ * bytes of slice histograms, rows * num_cand * 8 bytes of threshold-bin list
+ * entries and rows * num_cand * 4 bytes of their positions.  Returns 0 for
+ * arguments outside rows >= 0, num_cand >= 0, 1 <= parts <=
+ * DCP_TOPK_SPLIT_MAX_PARTS.
+ */
+DCP_TOPK_API size_t dcp_topk_select_split_workspace_bytes(int32_t rows, int32_t num_cand, int32_t parts);
+
+/*
+ * dcp_topk_select_split — dcp_topk_select with each row spread over `parts`
+ * workgroups, for batches of few rows.
+ *
+ * PR #50009 (Top-K performance) measures the merge at 1 to 64 decode rows,
+ * where one workgroup per row leaves most of the GPU's 256 compute units
+ * idle.  Here workgroup s of a row takes the candidates [s*L, (s+1)*L) with L
+ * = ceil(num_cand / parts) rounded up to a multiple of 64, and the row's
+ * workgroups exchange their pass-0 histograms and their threshold-bin items
+ * through `workspace` at two in-kernel barriers.  The result is the same as
+ * dcp_topk_select's, bit for bit.
+ *
+ *   cand, rows, num_cand, k, out   as for dcp_topk_select
+ *   parts            workgroups per row, 1 <= parts <= DCP_TOPK_SPLIT_MAX_PARTS,
+ *                    with L <= 8192
+ *   workspace        device, DCP_TOPK_WORKSPACE_ALIGN-aligned, at least
+ *                    dcp_topk_select_split_workspace_bytes(rows, num_cand,
+ *                    parts) bytes, overlapping neither cand nor out.  It must
+ *                    be zero-filled before its first use; every call leaves
+ *                    its counters at zero again, so it can be reused by later
+ *                    calls on the same stream.  Two calls in flight at once
+ *                    (on different streams) need different workspaces.
+ *   workspace_bytes  its size
+ *
+ * One cooperative launch of rows * parts workgroups, which must all be
+ * resident on the GPU at once: a larger grid returns DCP_TOPK_EUNSUPPORTED
+ * before anything runs (use dcp_topk_select there).  Rows with k >= num_cand
+ * need no selection and go through dcp_topk_select's kernel, which does not
+ * touch the workspace.  DCP_TOPK_EUNSUPPORTED also for parts or L out of
+ * range, DCP_TOPK_EWORKSPACE for a missing, short or misaligned workspace.
+ */
+DCP_TOPK_API int dcp_topk_select_split(const dcp_topk_cand* cand, int32_t rows, int32_t num_cand, int32_t k,
+                          int32_t parts, void* workspace, size_t workspace_bytes, dcp_topk_cand* out,
+                          hipStream_t stream);
+
 /*
  * dcp_topk_merge_workspace_bytes — workspace that dcp_topk_merge_chunked needs:
  * one chunk's row-major gathered buffer, min(rows, DCP_TOPK_MERGE_ROWS) * dcp *

@@ -25,6 +25,7 @@ MAX_CANDIDATES = 16384
 FUSED_MAX_RANKS = 16
 WORKSPACE_ALIGN = 256
 STATIC_SCRATCH_BYTES = 64 << 20
+SPLIT_MAX_PARTS = 8
 
 _lib = None
 
@@ -59,6 +60,10 @@ def open_library(path: str) -> ctypes.CDLL:
     lib.dcp_topk_pack.restype = ctypes.c_int
     lib.dcp_topk_select.argtypes = [vp, i32, i32, i32, vp, vp]
     lib.dcp_topk_select.restype = ctypes.c_int
+    lib.dcp_topk_select_split_workspace_bytes.argtypes = [i32, i32, i32]
+    lib.dcp_topk_select_split_workspace_bytes.restype = sz
+    lib.dcp_topk_select_split.argtypes = [vp, i32, i32, i32, i32, vp, sz, vp, vp]
+    lib.dcp_topk_select_split.restype = ctypes.c_int
     lib.dcp_topk_merge_workspace_bytes.argtypes = [i32, i32, i32]
     lib.dcp_topk_merge_workspace_bytes.restype = sz
     lib.dcp_topk_merge_chunked.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, vp, sz, vp, vp]
@@ -141,6 +146,38 @@ def select(cand: torch.Tensor, k: int, out: torch.Tensor | None = None) -> torch
         raise ValueError(f"out must be ({rows}, {k}, 2)")
     _check("dcp_topk_select",
            lib.dcp_topk_select(_p(cand.data_ptr()), rows, c, int(k), _p(out.data_ptr()), _stream(cand.device)))
+    return out
+
+
+def select_split_workspace_bytes(rows: int, num_cand: int, parts: int) -> int:
+    return int(load_library().dcp_topk_select_split_workspace_bytes(rows, num_cand, parts))
+
+
+def select_split_workspace(rows: int, num_cand: int, parts: int, device) -> torch.Tensor:
+    """A zero-filled workspace for ``select_split`` (reusable by later calls on
+    the same stream: every call leaves its counters at zero)."""
+    return torch.zeros(max(select_split_workspace_bytes(rows, num_cand, parts), 1), dtype=torch.uint8, device=device)
+
+
+def select_split(cand: torch.Tensor, k: int, parts: int, workspace: torch.Tensor | None = None,
+                 out: torch.Tensor | None = None) -> torch.Tensor:
+    """``select`` with each row spread over ``parts`` workgroups (for few rows)."""
+    lib = load_library()
+    _require(cand, "cand", torch.int32, 3)
+    rows, c, two = cand.shape
+    if two != 2:
+        raise ValueError("cand must be (rows, C, 2)")
+    if workspace is None:
+        workspace = select_split_workspace(rows, c, parts, cand.device)
+    _require(workspace, "workspace", torch.uint8, 1)
+    if out is None:
+        out = torch.empty((rows, max(int(k), 0), 2), dtype=torch.int32, device=cand.device)
+    _require(out, "out", torch.int32, 3)
+    if tuple(out.shape) != (rows, k, 2):
+        raise ValueError(f"out must be ({rows}, {k}, 2)")
+    _check("dcp_topk_select_split",
+           lib.dcp_topk_select_split(_p(cand.data_ptr()), rows, c, int(k), int(parts), _p(workspace.data_ptr()),
+                                     workspace.numel(), _p(out.data_ptr()), _stream(cand.device)))
     return out
 
 

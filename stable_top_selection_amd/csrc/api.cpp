@@ -186,6 +186,35 @@ int dcp_topk_select(const dcp_topk_cand* cand, int32_t rows, int32_t num_cand, i
   return hip_status(dcptopk::launch_select(cand, rows, num_cand, k, out, stream));
 }
 
+size_t dcp_topk_select_split_workspace_bytes(int32_t rows, int32_t num_cand, int32_t parts) {
+  if (rows < 0 || num_cand < 0 || parts < 1 || parts > DCP_TOPK_SPLIT_MAX_PARTS) return 0;
+  return dcptopk::split_layout(rows, num_cand, parts).bytes;
+}
+
+int dcp_topk_select_split(const dcp_topk_cand* cand, int32_t rows, int32_t num_cand, int32_t k, int32_t parts,
+                          void* workspace, size_t workspace_bytes, dcp_topk_cand* out, hipStream_t stream) {
+  int st = check_select(cand, rows, num_cand, k, out);
+  if (st != DCP_TOPK_OK || rows == 0) return st;
+  if (parts < 1 || parts > DCP_TOPK_SPLIT_MAX_PARTS || dcptopk::split_slice_len(num_cand, parts) > dcptopk::kSplitMaxSlice)
+    return DCP_TOPK_EUNSUPPORTED;
+  if (k >= num_cand) return hip_status(dcptopk::launch_select(cand, rows, num_cand, k, out, stream));
+  const size_t need = dcp_topk_select_split_workspace_bytes(rows, num_cand, parts);
+  if (workspace == nullptr || !aligned(workspace, DCP_TOPK_WORKSPACE_ALIGN) || workspace_bytes < need)
+    return DCP_TOPK_EWORKSPACE;
+  const Span ws{reinterpret_cast<uintptr_t>(workspace), need};
+  Span in_span, out_span;
+  if (!strided_span(cand, rows, num_cand, num_cand, kCandBytes, &in_span) ||
+      !strided_span(out, rows, k, k, kCandBytes, &out_span))
+    return DCP_TOPK_EINVAL;
+  if (overlap(ws, in_span) || overlap(ws, out_span)) return DCP_TOPK_EINVAL;
+  const hipError_t e = dcptopk::launch_select_split(cand, rows, num_cand, k, parts, workspace, out, stream);
+  if (e == hipErrorCooperativeLaunchTooLarge) {
+    (void)hipGetLastError();  // clear the rejected launch's error (it enqueued nothing) for later callers
+    return DCP_TOPK_EUNSUPPORTED;
+  }
+  return hip_status(e);
+}
+
 int dcp_topk_pack(const float* local_scores, const int32_t* local_idx, int64_t src_row_stride,
                   const int32_t* row_starts, int32_t rank_offset, int32_t rows, int32_t local_k, dcp_topk_cand* dst,
                   int64_t dst_row_stride, hipStream_t stream) {

@@ -14,6 +14,46 @@ namespace dcptopk {
 hipError_t launch_select(const dcp_topk_cand* cand, int32_t rows, int32_t num_cand, int32_t k,
                          dcp_topk_cand* out, hipStream_t stream);
 
+// Split-row select: the caller's workspace, per row, holds four counters, one
+// pass-0 histogram per slice (kSplitHistWords words: the 2048 bin counts, then
+// the slice's padding count and 7 spare words), and the row's threshold-bin
+// list (num_cand (key, id) pairs and num_cand positions).  Regions start on
+// 256-byte boundaries.
+constexpr int kSplitMaxParts = 8;
+constexpr int kSplitHistWords = 2048 + 8;
+constexpr int kSplitMaxSlice = 8192;  // most candidates one workgroup of a split row holds
+
+struct SplitLayout {
+  size_t ctrl, hist, list, pos, bytes;  // byte offsets of the regions, total bytes
+};
+
+inline size_t split_round_up(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+inline SplitLayout split_layout(int64_t rows, int64_t num_cand, int64_t parts) {
+  SplitLayout l;
+  l.ctrl = 0;
+  l.hist = split_round_up(static_cast<size_t>(rows) * 4 * sizeof(uint32_t));
+  l.list = l.hist + split_round_up(static_cast<size_t>(rows * parts) * kSplitHistWords * sizeof(uint32_t));
+  l.pos = l.list + split_round_up(static_cast<size_t>(rows * num_cand) * 2 * sizeof(uint32_t));
+  l.bytes = l.pos + split_round_up(static_cast<size_t>(rows * num_cand) * sizeof(uint32_t));
+  return l;
+}
+
+// Candidates per slice when a row of num_cand is split `parts` ways: the
+// even share rounded up to a multiple of 64.
+inline int64_t split_slice_len(int64_t num_cand, int64_t parts) {
+  return ((num_cand + parts - 1) / parts + 63) / 64 * 64;
+}
+
+// Enqueue the split-row select (one cooperative launch of rows * parts
+// workgroups).  Arguments are already validated: 1 <= parts <=
+// kSplitMaxParts, 1 <= k < num_cand, split_slice_len(num_cand, parts) <=
+// kSplitMaxSlice, a workspace of split_layout(...).bytes bytes, 256-byte
+// aligned, whose counters are zero.  Returns hipErrorCooperativeLaunchTooLarge
+// when the grid cannot be resident at once.
+hipError_t launch_select_split(const dcp_topk_cand* cand, int32_t rows, int32_t num_cand, int32_t k, int32_t parts,
+                               void* workspace, dcp_topk_cand* out, hipStream_t stream);
+
 // One rank's inputs to the pack kernel.
 struct PackRank {
   const float* scores;

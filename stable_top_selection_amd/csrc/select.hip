@@ -69,6 +69,7 @@ constexpr int kBins = 2048;      // widest digit: 11 bits
 constexpr int kSmallBins = 256;  // list passes: digits of at most 8 bits
 constexpr int kListCap = 2048;   // largest threshold bucket handled as a list
 constexpr int kBucket = 8;       // items a list pass keeps per digit; smaller sub-bins finish by comparison
+constexpr int kMaxSplit = kSplitMaxParts;  // most workgroups one row is split over (split-row select)
 constexpr uint32_t kBufferWord3 = 0x00020000u;  // raw buffer resource, gfx9 family
 constexpr uint32_t kDropOffset = 0x80000000u;   // beyond any num_records used here
 // Cache policy of the candidate loads and of the 8-byte result stores:
@@ -289,6 +290,8 @@ struct alignas(16) SelectLds {
   uint2 list[kListCap + 1];        // (key, id) of the items in the pass-0 threshold bin, then
                                    // one write-only dump slot for all other items
   uint32_t segment[2][kWaves];     // per-wave flagged counts (dup scan, select scan)
+  uint32_t slices[3][kMaxSplit];   // split rows: per slice, keys above the threshold bin, selected
+                                   // keys of the bin other than full duplicates, full duplicates
   uint32_t sink[kWave];            // per-lane target of atomics whose item does not count
   uint32_t common[4];              // OR / AND of the list's keys and of its complemented ids
 };
@@ -1208,6 +1211,348 @@ __global__ __launch_bounds__(BLOCK) void stable_topk_kernel(Source src, Sink sin
   }
 }
 
+// ---------------------------------------------------------------------------
+// Split-row select, for batches of few rows: one workgroup per row leaves most
+// CUs idle, so here `parts` workgroups share a row.  Workgroup s of a row takes
+// its slice, the candidates [s*L, (s+1)*L), and the row's workgroups exchange
+// what they need through the caller's workspace at two row barriers:
+//   1. every slice's pass-0 histogram: after the barrier every workgroup sums
+//      them and finds the threshold bin (the same one everywhere);
+//   2. every slice's items of that bin, with their positions, appended to the
+//      row's list: after the barrier every workgroup resolves the exact
+//      threshold from the list (radix passes), and counts from the slices'
+//      histograms and the list how many items the earlier slices select, so
+//      that it knows its output offset without a third exchange.
+// Then each workgroup writes its slice's selected items, in position order, at
+// that offset.  The launch is cooperative (the runtime guarantees that every
+// workgroup of the grid is resident), so the row barriers always complete;
+// they still give up after a bounded number of polls.  The workspace's
+// per-row counters start at zero and the last workgroup of a row to finish
+// sets them back to zero.
+// ---------------------------------------------------------------------------
+constexpr int kSplitHist = kSplitHistWords;  // words per slice histogram: kBins counts, then the padding count
+static_assert(kSplitHistWords == kBins + 8, "slice histogram layout");
+constexpr int kSplitSpin = 1 << 20;    // polls of a row barrier before it gives up
+
+struct SplitWorkspace {
+  uint32_t* ctrl;   // per row: arrivals at barrier 1, at barrier 2, list length, finished workgroups
+  uint32_t* hist;   // per row and slice: kSplitHist words
+  uint2* list;      // per row: num_cand (key, id) entries
+  uint32_t* pos;    // per row: num_cand positions
+};
+
+// Every thread of the workgroup: its global writes so far are visible to the
+// row's other workgroups, and theirs, written before they arrived, to it.
+// One thread arrives with a release add and polls with relaxed loads (an
+// acquire load per poll would invalidate the caches on every poll), then
+// takes one acquire fence; the workgroup barriers on either side order the
+// other threads' writes before the arrival and their reads after the fence.
+__device__ __forceinline__ void row_barrier(uint32_t* counter, uint32_t parts, int t) {
+  __syncthreads();
+  if (t == 0) {
+    __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    int spin = 0;
+    while (__hip_atomic_load(counter, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < parts && ++spin < kSplitSpin)
+      __builtin_amdgcn_s_sleep(1);
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  }
+  __syncthreads();
+}
+
+// A radix pass over the row's list in the workspace (the threshold bin's m
+// items): the digit at SHIFT (BITS wide) of the keys (BY_ID false) or of the
+// complemented ids of the items whose key is thr, among those that match st;
+// hist[p % 3] rotation as in radix_pass.
+template <int BLOCK, int SHIFT, int BITS, bool BY_ID>
+__device__ __forceinline__ void split_list_pass(SelectLds<BLOCK>& lds, int p, const uint2* list, uint32_t m,
+                                                uint32_t thr, Radix& st, int t, int lane) {
+  constexpr int NB = 1 << BITS;
+  constexpr uint32_t kDigitMask = NB - 1;
+  uint32_t* hist = lds.hist[p % 3];
+  for (uint32_t e = static_cast<uint32_t>(t); e < m; e += BLOCK) {
+    const uint2 x = list[e];
+    const uint32_t v = BY_ID ? ~x.y : x.x;
+    if ((!BY_ID || x.x == thr) && (v & st.mask) == st.prefix) lds_add(hist + ((v >> SHIFT) & kDigitMask));
+  }
+  lds_barrier();
+  clear_words<BLOCK>(lds.hist[(p + 2) % 3], kBins, t);
+  advance(st, find_digit<NB>(hist, st.need, lane), SHIFT, kDigitMask);
+}
+
+template <int BLOCK, int VEC, int N>
+__global__ __launch_bounds__(BLOCK) void split_select_kernel(const dcp_topk_cand* __restrict__ cand, int32_t num_cand,
+                                                             int32_t k, int32_t parts, int32_t slice_len,
+                                                             SplitWorkspace ws, dcp_topk_cand* __restrict__ out) {
+  constexpr int NV = N / VEC;
+  constexpr int kChunk = VEC * kWave;
+  __shared__ SelectLds<BLOCK> lds;
+  constexpr int kStageCap = kWave * N / 2 < 448 ? kWave * N / 2 : 448;
+  __shared__ uint2 stage[BLOCK / kWave][kStageCap + kWave];
+
+  const int t = threadIdx.x;
+  const int lane = t & (kWave - 1);
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int64_t row = blockIdx.x / parts;
+  const int s = static_cast<int>(blockIdx.x % parts);
+  const int start = s * slice_len;  // the slice's first position in the row
+  const int len = num_cand - start < slice_len ? num_cand - start : slice_len;  // its candidates (>= 0)
+  uint32_t* ctrl = ws.ctrl + row * 4;
+  uint32_t* hist_g = ws.hist + row * parts * kSplitHist;
+  uint2* list = ws.list + row * num_cand;
+  uint32_t* lpos = ws.pos + row * num_cand;
+  const PairSink::Row dst = PairSink{out, k}.bind(row, k);
+
+  // the slice's candidates: wave w holds [w*64*N, (w+1)*64*N) of the slice,
+  // 64*VEC consecutive ones per load, like the one-workgroup kernel
+  const int first = w * kWave * N + VEC * lane;
+  const int room = len - first;  // this thread's items are valid below this offset
+  auto ok = [&](int i) -> bool { return (i / VEC) * kChunk + i % VEC < room; };
+  uint32_t bits[N], idv[N];
+  {
+    const __amdgpu_buffer_rsrc_t src = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<dcp_topk_cand*>(cand + row * num_cand + start), 0,
+        (len > 0 ? len : 0) * static_cast<int>(sizeof(dcp_topk_cand)), static_cast<int>(kBufferWord3));
+    const int voff = first * static_cast<int>(sizeof(dcp_topk_cand));
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+      const int soff = v * kChunk * static_cast<int>(sizeof(dcp_topk_cand));
+      if constexpr (VEC == 2) {
+        const int4 x = __builtin_bit_cast(int4, __builtin_amdgcn_raw_buffer_load_b128(src, voff, soff, kLoadPolicy));
+        bits[2 * v] = x.x;
+        idv[2 * v] = x.y;
+        bits[2 * v + 1] = x.z;
+        idv[2 * v + 1] = x.w;
+      } else {
+        const int2v x = __builtin_amdgcn_raw_buffer_load_b64(src, voff, soff, kLoadPolicy);
+        bits[v] = x.x;
+        idv[v] = x.y;
+      }
+    }
+  }
+  clear_words<BLOCK>(&lds.hist[0][0], 3 * kBins + 3 * kSmallBins + kPadWords, t);
+  if (t < 4) lds.common[t] = (t & 1) ? ~0u : 0u;
+  if (t < 3 * kMaxSplit) (&lds.slices[0][0])[t] = 0u;
+  lds_barrier();
+
+  // pass 0 over the slice (padding keys in per-lane words, as in the
+  // one-workgroup kernel), then the slice's histogram to the workspace
+  uint32_t key[N];
+  uint32_t* pad_word = lds.padcnt + (lane % kPadWords);
+  uint32_t* spare = lds.sink + lane;
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    key[i] = score_key(bits[i]);
+    uint32_t* target = key[i] == kPadKey ? pad_word : lds.hist[0] + (key[i] >> 21);
+    lds_add(ok(i) ? target : spare);
+  }
+  lds_barrier();
+  uint32_t* my_hist = hist_g + s * kSplitHist;
+  for (int b = 4 * t; b < kBins; b += 4 * BLOCK)
+    *reinterpret_cast<uint4*>(my_hist + b) = *reinterpret_cast<const uint4*>(lds.hist[0] + b);
+  if (t == 0) {
+    uint32_t pads = 0u;
+#pragma unroll
+    for (int j = 0; j < kPadWords; ++j) pads += lds.padcnt[j];
+    my_hist[kBins] = pads;
+  }
+  row_barrier(ctrl + 0, static_cast<uint32_t>(parts), t);
+
+  // the row's histogram: the sum of the slices'
+  for (int b = 4 * t; b < kBins; b += 4 * BLOCK) {
+    uint4 acc = make_uint4(0u, 0u, 0u, 0u);
+    for (int q = 0; q < parts; ++q) {
+      const uint4 x = *reinterpret_cast<const uint4*>(hist_g + q * kSplitHist + b);
+      acc.x += x.x;
+      acc.y += x.y;
+      acc.z += x.z;
+      acc.w += x.w;
+    }
+    *reinterpret_cast<uint4*>(lds.hist[0] + b) = acc;
+  }
+  uint32_t pad_total = 0u;
+  for (int q = 0; q < parts; ++q) pad_total += hist_g[q * kSplitHist + kBins];
+  pad_total = uniform(pad_total);
+  lds_barrier();
+  Radix sk{0u, 0u, static_cast<uint32_t>(k), 0u};
+  advance(sk, find_digit_pass0(lds.hist[0], sk.need, lane, kPadBin, pad_total), 21, 0x7FFu);
+  const uint32_t d0 = sk.prefix >> 21;
+  const bool listed = sk.count != sk.need;  // the threshold is inside bin d0: its items go to the list
+
+  // this slice's items of bin d0 to the row's list (one global atomic per
+  // wave for the wave's range)
+  if (listed) {
+    uint32_t mine = 0u;
+#pragma unroll
+    for (int i = 0; i < N; ++i) mine += static_cast<uint32_t>(__popcll(__ballot(ok(i) && (key[i] >> 21) == d0)));
+    uint32_t base = 0u;
+    if (lane == 0) base = __hip_atomic_fetch_add(ctrl + 2, mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    base = lane_of(base, 0);
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const bool in = ok(i) && (key[i] >> 21) == d0;
+      const uint64_t m = __ballot(in);
+      const uint32_t e = base + __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m >> 32),
+                                                          __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0u));
+      if (in && e < static_cast<uint32_t>(num_cand)) {  // (always, unless the workspace was not zeroed)
+        list[e] = make_uint2(key[i], idv[i]);
+        lpos[e] = static_cast<uint32_t>(start + first + (i / VEC) * kChunk + i % VEC);
+      }
+      base += static_cast<uint32_t>(__popcll(m));
+    }
+  }
+  row_barrier(ctrl + 1, static_cast<uint32_t>(parts), t);
+
+  // the exact threshold from the list: the bits its items share first (a
+  // list of identical keys needs no key pass, one of identical (key, id)
+  // pairs, such as padding, no id pass), then radix passes from the highest
+  // bit where they differ
+  bool tie = false, dup = false;
+  Radix ik{0u, 0u, 0u, 0u};
+  // (a workspace that was not zeroed gives wrong results, never an access
+  // outside it: the list length and the slice indexes are clamped)
+  const uint32_t m = listed ? min(uniform(__hip_atomic_load(ctrl + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)),
+                                  static_cast<uint32_t>(num_cand))
+                            : 0u;
+  if (listed) {
+    uint32_t a = 0u, b = ~0u, c = 0u, e = ~0u;
+    for (uint32_t q = static_cast<uint32_t>(t); q < m; q += BLOCK) {
+      const uint2 x = list[q];
+      a |= x.x;
+      b &= x.x;
+      c |= ~x.y;
+      e &= ~x.y;
+    }
+    uint32_t kor, kand, uor, uand;
+    block_common_bits(lds, lane, a, b, c, e, kor, kand, uor, uand);
+    int p = 1;
+    if (kor == kand) {
+      sk.prefix = kor;
+      sk.mask = ~0u;
+    } else {
+      do {
+        split_list_pass<BLOCK, 10, 11, false>(lds, p++, list, m, 0u, sk, t, lane);
+        if (sk.count == sk.need) break;
+        split_list_pass<BLOCK, 0, 10, false>(lds, p++, list, m, 0u, sk, t, lane);
+      } while (false);
+    }
+    tie = sk.count > sk.need;
+    if (tie) {
+      ik.need = sk.need;
+      ik.count = sk.count;
+      const uint32_t differ = uor ^ uand;
+      if (differ == 0u) {
+        ik.prefix = uand;
+        ik.mask = ~0u;
+      } else {
+        const int hb = 31 - __builtin_clz(differ);
+        if (hb < 31) {
+          ik.mask = ~0u << (hb + 1);
+          ik.prefix = uand & ik.mask;
+        }
+        do {
+          if (hb >= 21) {
+            split_list_pass<BLOCK, 21, 11, true>(lds, p++, list, m, sk.prefix, ik, t, lane);
+            if (ik.count == ik.need) break;
+          }
+          if (hb >= 10) {
+            split_list_pass<BLOCK, 10, 11, true>(lds, p++, list, m, sk.prefix, ik, t, lane);
+            if (ik.count == ik.need) break;
+          }
+          split_list_pass<BLOCK, 0, 10, true>(lds, p++, list, m, sk.prefix, ik, t, lane);
+        } while (false);
+      }
+      dup = ik.count > ik.need;
+    }
+  }
+
+  // per slice: keys above bin d0 (from the slices' histograms), selected keys
+  // of bin d0 other than full duplicates, and full duplicates (from the list)
+  const uint32_t thr = sk.prefix;
+  auto selected = [&](uint32_t kk, uint32_t u) -> bool {  // not counting full duplicates
+    if (!tie) return kk >= thr;
+    return kk > thr || (kk == thr && (dup ? u > ik.prefix : u >= ik.prefix));
+  };
+  // wave q counts slice q's keys above bin d0 (and, when the whole bin is
+  // taken, the bin itself); padding keys count here unless they are listed
+  if (w < parts) {
+    const uint32_t* h = hist_g + w * kSplitHist;
+    uint32_t above = 0u;
+    for (int b = lane; b < kBins; b += kWave) above += static_cast<uint32_t>(b) > d0 || (!listed && b == d0) ? h[b] : 0u;
+    above = lane_of(wave_inclusive_scan(above, lane), kWave - 1);
+    if (kPadBin > d0 || (kPadBin == d0 && !listed)) above += h[kBins];
+    if (lane == 0) lds.slices[0][w] = above;
+  }
+  for (uint32_t q = static_cast<uint32_t>(t); q < m; q += BLOCK) {
+    const uint2 x = list[q];
+    const uint32_t sq = min(lpos[q] / static_cast<uint32_t>(slice_len), static_cast<uint32_t>(kMaxSplit - 1));
+    const uint32_t u = ~x.y;
+    if (selected(x.x, u)) lds_add(&lds.slices[1][sq]);
+    if (dup && x.x == thr && u == ik.prefix) lds_add(&lds.slices[2][sq]);
+  }
+  lds_barrier();
+  uint32_t out_base = 0u, dup_before = 0u;
+  for (int q = 0; q < s; ++q) {
+    const uint32_t dq = lds.slices[2][q];
+    const uint32_t left = ik.need > dup_before ? ik.need - dup_before : 0u;  // duplicates still to take
+    out_base += lds.slices[0][q] + lds.slices[1][q] + (dup ? (dq < left ? dq : left) : 0u);
+    dup_before += dq;
+  }
+  out_base = uniform(out_base);
+  dup_before = uniform(dup_before);
+
+  // this slice's selection and its compaction, as in the one-workgroup kernel
+  uint32_t sel[N];
+  if (dup) {
+    uint32_t same[N], duprank[N];
+#pragma unroll
+    for (int i = 0; i < N; ++i) same[i] = (ok(i) && key[i] == thr && ~idv[i] == ik.prefix) ? 1u : 0u;
+    position_rank<BLOCK, VEC, N>(same, lds.segment[0], duprank, lane, w);
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const uint32_t u = ~idv[i];
+      const bool wins = u > ik.prefix || (u == ik.prefix && dup_before + duprank[i] < ik.need);
+      sel[i] = (ok(i) && (key[i] > thr || (key[i] == thr && wins))) ? 1u : 0u;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < N; ++i) sel[i] = (ok(i) && selected(key[i], ~idv[i])) ? 1u : 0u;
+  }
+  uint32_t rank[N];
+  const uint32_t out_count = wave_rank<VEC, N>(sel, rank, lane);
+  if (lane == 0) lds.segment[1][w] = out_count;
+  const bool staged = out_count <= static_cast<uint32_t>(kStageCap);
+  if (staged) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) stage[w][sel[i] ? rank[i] : static_cast<uint32_t>(kStageCap)] = make_uint2(bits[i], idv[i]);
+  }
+  lds_barrier();
+  const uint32_t out_first = out_base + waves_before<BLOCK>(lds.segment[1], w);
+  if (staged) {
+    constexpr int kCopies = (kStageCap + kWave - 1) / kWave;
+    uint2 x[kCopies];
+#pragma unroll
+    for (int u = 0; u < kCopies; ++u) x[u] = stage[w][u * kWave + lane];
+#pragma unroll
+    for (int u = 0; u < kCopies; ++u) {
+      const uint32_t e = static_cast<uint32_t>(u * kWave + lane);
+      dst.store(e < out_count, out_first + e, x[u].x, x[u].y);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < N; ++i) dst.store(sel[i] != 0u, out_first + rank[i], bits[i], idv[i]);
+  }
+
+  // the last workgroup of the row to finish resets the row's counters
+  __syncthreads();
+  if (t == 0 && __hip_atomic_fetch_add(ctrl + 3, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT) ==
+                    static_cast<uint32_t>(parts) - 1u) {
+    ctrl[0] = 0u;
+    ctrl[1] = 0u;
+    ctrl[2] = 0u;
+    __hip_atomic_store(ctrl + 3, 0u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
 // full: every row has exactly BLOCK*N candidates, so no item is masked out
 template <int BLOCK, int VEC, int N, class Source, class Sink>
 hipError_t launch(const Source& src, const Sink& sink, bool uniform_rows, int32_t rows, int32_t num_cand, int32_t k,
@@ -1298,6 +1643,50 @@ hipError_t launch_local(const float* scores, int64_t score_row_stride, const int
   if (fits(4)) return launch_sized<4>(src, sink, uniform_rows, rows, num_cols, k, stream);
   if (fits(2)) return launch_sized<2>(src, sink, uniform_rows, rows, num_cols, k, stream);
   return launch_sized<1>(src, sink, uniform_rows, rows, num_cols, k, stream);
+}
+
+namespace {
+
+template <int VEC, int N>
+hipError_t launch_split_sized(const dcp_topk_cand* cand, int32_t rows, int32_t num_cand, int32_t k, int32_t parts,
+                              int32_t slice_len, const SplitWorkspace& ws, dcp_topk_cand* out, hipStream_t stream) {
+  auto kernel = split_select_kernel<512, VEC, N>;
+  // every workgroup of the grid must be resident at once (the row barriers
+  // wait for all of a row's workgroups); checked here rather than left to the
+  // runtime
+  int device = 0, cus = 0, per_cu = 0;
+  hipError_t e = hipGetDevice(&device);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device);
+  if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 512, 0);
+  if (e != hipSuccess) return e;
+  if (static_cast<int64_t>(rows) * parts > static_cast<int64_t>(cus) * per_cu) return hipErrorCooperativeLaunchTooLarge;
+  void* args[] = {const_cast<dcp_topk_cand**>(&cand), &num_cand, &k, &parts, &slice_len,
+                  const_cast<SplitWorkspace*>(&ws), &out};
+  return hipLaunchCooperativeKernel(reinterpret_cast<const void*>(kernel), dim3(static_cast<uint32_t>(rows * parts)),
+                                    dim3(512), args, 0, stream);
+}
+
+template <int VEC>
+hipError_t launch_split_vec(const dcp_topk_cand* cand, int32_t rows, int32_t num_cand, int32_t k, int32_t parts,
+                            int32_t slice_len, const SplitWorkspace& ws, dcp_topk_cand* out, hipStream_t stream) {
+  if (slice_len <= 512 * 4) return launch_split_sized<VEC, 4>(cand, rows, num_cand, k, parts, slice_len, ws, out, stream);
+  static_assert(kSplitMaxSlice == 512 * 16, "the widest split kernel holds 16 items per thread");
+  if (slice_len <= 512 * 8) return launch_split_sized<VEC, 8>(cand, rows, num_cand, k, parts, slice_len, ws, out, stream);
+  return launch_split_sized<VEC, 16>(cand, rows, num_cand, k, parts, slice_len, ws, out, stream);
+}
+
+}  // namespace
+
+hipError_t launch_select_split(const dcp_topk_cand* cand, int32_t rows, int32_t num_cand, int32_t k, int32_t parts,
+                               void* workspace, dcp_topk_cand* out, hipStream_t stream) {
+  const SplitLayout l = split_layout(rows, num_cand, parts);
+  char* base = static_cast<char*>(workspace);
+  const SplitWorkspace ws{reinterpret_cast<uint32_t*>(base + l.ctrl), reinterpret_cast<uint32_t*>(base + l.hist),
+                          reinterpret_cast<uint2*>(base + l.list), reinterpret_cast<uint32_t*>(base + l.pos)};
+  const int32_t slice_len = static_cast<int32_t>(split_slice_len(num_cand, parts));
+  if ((num_cand % 2 == 0) && (reinterpret_cast<uintptr_t>(cand) % 16 == 0))
+    return launch_split_vec<2>(cand, rows, num_cand, k, parts, slice_len, ws, out, stream);
+  return launch_split_vec<1>(cand, rows, num_cand, k, parts, slice_len, ws, out, stream);
 }
 
 }  // namespace dcptopk

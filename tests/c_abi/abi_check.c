@@ -27,6 +27,13 @@ int main(void) {
   expect("select, k = 0", dcp_topk_select(fake_in, 1, 8192, 0, fake_out, NULL), DCP_TOPK_EINVAL);
   expect("select, too many candidates", dcp_topk_select(fake_in, 1, DCP_TOPK_MAX_CANDIDATES + 1, 1, fake_out, NULL),
          DCP_TOPK_EUNSUPPORTED);
+  expect("split workspace bytes, 1 row, 8192 candidates, 2 parts",
+         (long)dcp_topk_select_split_workspace_bytes(1, 8192, 2), 256L + 16640L + 65536L + 32768L);
+  expect("split select, parts past the limit",
+         dcp_topk_select_split(fake_in, 1, 8192, 2048, DCP_TOPK_SPLIT_MAX_PARTS + 1, NULL, 0, fake_out, NULL),
+         DCP_TOPK_EUNSUPPORTED);
+  expect("split select, no workspace", dcp_topk_select_split(fake_in, 1, 8192, 2048, 2, NULL, 0, fake_out, NULL),
+         DCP_TOPK_EWORKSPACE);
   expect("pack, no rows", dcp_topk_pack(NULL, NULL, 0, NULL, 0, 0, 16, NULL, 0, NULL), DCP_TOPK_OK);
   {
     const float* sc[1] = {(const float*)(uintptr_t)0x7F0020000000ull};

@@ -15,12 +15,15 @@ def to_dev(a: np.ndarray) -> torch.Tensor:
     return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
 
 
-def gpu_select(scores: np.ndarray, ids: np.ndarray, k: int, guard: int = 0, misalign: bool = False):
+def gpu_select(scores: np.ndarray, ids: np.ndarray, k: int, guard: int = 0, misalign: bool = False,
+               split_parts: int = 0, workspace: torch.Tensor | None = None):
     """Select on the GPU; returns (score bits uint32, ids int32), each (rows, k).
 
     ``guard`` rows of canary candidates are placed before and after the output
     and must survive untouched; ``misalign`` starts the candidate buffer 8
-    bytes past a 16-byte boundary (the 8-byte load path)."""
+    bytes past a 16-byte boundary (the 8-byte load path).  ``split_parts`` > 0
+    selects through the split-row entry point with that many workgroups per
+    row (in ``workspace`` if given, else a fresh zeroed one)."""
     rows, c = scores.shape
     inter = np.empty((rows, c, 2), np.int32)
     inter[..., 0] = scores.view(np.int32)
@@ -35,7 +38,10 @@ def gpu_select(scores: np.ndarray, ids: np.ndarray, k: int, guard: int = 0, misa
     canary = torch.tensor([0x5EED5EED, 0x0BADF00D], dtype=torch.int32, device=DEV)
     big = canary.repeat((rows + 2 * guard) * k).view(rows + 2 * guard, k, 2) if k > 0 else None
     out = big[guard:guard + rows]
-    B.select(cand, k, out=out)
+    if split_parts:
+        B.select_split(cand, k, split_parts, workspace=workspace, out=out)
+    else:
+        B.select(cand, k, out=out)
     torch.cuda.synchronize()
     if guard:
         g = big.cpu().numpy()

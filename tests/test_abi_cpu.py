@@ -25,7 +25,8 @@ def test_exports_every_header_function(lib):
     names = B.header_functions()
     assert set(names) == {"dcp_topk_pack", "dcp_topk_select", "dcp_topk_merge_workspace_bytes",
                           "dcp_topk_merge_chunked", "dcp_topk_merge_chunked_static", "dcp_topk_merge_fused",
-                          "dcp_topk_local", "dcp_topk_status_string"}
+                          "dcp_topk_local", "dcp_topk_status_string", "dcp_topk_select_split",
+                          "dcp_topk_select_split_workspace_bytes"}
     for n in names:
         assert hasattr(lib, n), n
     exported = subprocess.run(["nm", "-D", "--defined-only", LIB_PATH], capture_output=True, text=True).stdout
@@ -171,3 +172,39 @@ def test_local_argument_checks(lib):
     assert loc(*args(o2=os_ + 4)) == B.EINVAL  # the two outputs overlap
     assert loc(*args(o1=a + 4096 * 4)) == B.EINVAL  # score output inside the scores
     assert loc(*args(ln=oi + 64)) == B.EINVAL  # lengths inside the index output
+
+
+def _split_bytes(rows, num_cand, parts):
+    """The split workspace as the header describes it: four regions, each
+    rounded up to 256 bytes."""
+    up = lambda x: (x + 255) // 256 * 256
+    return up(rows * 16) + up(rows * parts * 8224) + up(rows * num_cand * 8) + up(rows * num_cand * 4)
+
+
+@pytest.mark.parametrize("rows,num_cand,parts", [(0, 8192, 4), (1, 8192, 1), (16, 8192, 4), (64, 8192, 8),
+                                                 (3, 1000, 3), (5, 16384, 2), (1, 0, 2)])
+def test_split_workspace_bytes(lib, rows, num_cand, parts):
+    assert lib.dcp_topk_select_split_workspace_bytes(rows, num_cand, parts) == _split_bytes(rows, num_cand, parts)
+
+
+def test_split_workspace_bytes_rejects_bad_arguments(lib):
+    f = lib.dcp_topk_select_split_workspace_bytes
+    assert f(-1, 8192, 4) == 0 and f(1, -1, 4) == 0 and f(1, 8192, 0) == 0 and f(1, 8192, 9) == 0
+
+
+def test_select_split_argument_checks(lib):
+    s = lib.dcp_topk_select_split
+    ws = 0x7F0020000000
+    need = _split_bytes(16, 8192, 4)
+    assert s(None, 0, 8192, 2048, 4, None, 0, None, None) == B.OK  # no rows
+    assert s(None, 16, 8192, 2048, 4, P(ws), need, P(DEV_B), None) == B.EINVAL  # null input
+    assert s(P(DEV_A), 16, 8192, 0, 4, P(ws), need, P(DEV_B), None) == B.EINVAL  # k < 1
+    assert s(P(DEV_A), 16, 8192, 2048, 0, P(ws), need, P(DEV_B), None) == B.EUNSUPPORTED  # parts < 1
+    assert s(P(DEV_A), 16, 8192, 2048, 9, P(ws), need, P(DEV_B), None) == B.EUNSUPPORTED  # parts > 8
+    assert s(P(DEV_A), 1, 16384, 2048, 1, P(ws), 1 << 30, P(DEV_B), None) == B.EUNSUPPORTED  # slice > 8192
+    assert s(P(DEV_A), 16, 8192, 2048, 4, None, need, P(DEV_B), None) == B.EWORKSPACE
+    assert s(P(DEV_A), 16, 8192, 2048, 4, P(ws + 8), need, P(DEV_B), None) == B.EWORKSPACE  # misaligned
+    assert s(P(DEV_A), 16, 8192, 2048, 4, P(ws), need - 1, P(DEV_B), None) == B.EWORKSPACE  # short
+    # workspace overlapping the input or the output
+    assert s(P(DEV_A), 16, 8192, 2048, 4, P(DEV_A + 4096), need, P(DEV_B), None) == B.EINVAL
+    assert s(P(DEV_A), 16, 8192, 2048, 4, P(DEV_B - 256), need, P(DEV_B), None) == B.EINVAL

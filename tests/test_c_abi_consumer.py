@@ -26,4 +26,4 @@ def test_plain_c_consumer(tmp_path):
     r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120)
     assert r.returncode == 0, r.stdout + r.stderr
     assert "FAIL" not in r.stdout
-    assert r.stdout.count("ok  ") == 13
+    assert r.stdout.count("ok  ") == 16

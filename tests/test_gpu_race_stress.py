@@ -17,7 +17,7 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_helpers import assert_select_parity, to_dev
+from gpu_helpers import assert_select_parity, gpu_select, to_dev
 from oracle import stable_topk as O
 from stable_top_selection_amd import binding as B
 from stable_top_selection_amd import build as BLD
@@ -115,3 +115,17 @@ def test_local_topk():
     ws, wi = O.local_topk(d.scores, d.k, d.lengths)
     assert np.array_equal(os_.cpu().numpy().view(np.uint32), ws.view(np.uint32))
     assert np.array_equal(oi.cpu().numpy(), wi)
+
+
+@pytest.mark.parametrize("make,parts", [(lambda: W.decode(16), 4), (lambda: W.tie_heavy(rows=16, seed=42), 8),
+                                        (lambda: W.random_gathered(8, 8192, 2048, seed=943, dist="const",
+                                                                   id_span=64, repeat_ids=True), 4)],
+                         ids=["decode_16_parts4", "tie_heavy_parts8", "duplicates_parts4"])
+def test_split_rows(make, parts):
+    """The split-row select: its workgroup barriers under delayed waves, with
+    the row barriers between workgroups in between."""
+    g = make()
+    print(f"[race stress] split rows {g.name} parts={parts}", flush=True)
+    gb, gi = gpu_select(g.scores, g.ids, g.k, split_parts=parts)
+    os_, oi = O.select(g.scores, g.ids, g.k)
+    assert np.array_equal(gb, os_.view(np.uint32)) and np.array_equal(gi, oi)
