@@ -21,6 +21,10 @@ LIB_PATH = os.path.join(PKG, LIB_NAME)
 # (DCPTOPK_RACE_STRESS), for the race-stress tests only
 STRESS_LIB_PATH = os.path.join(PKG, "libdcptopk_race_stress.so")
 STRESS_FLAGS = ["-DDCPTOPK_RACE_STRESS=1"]
+# the same library with shader-clock stamps at the select kernel's phase
+# boundaries (DCPTOPK_PHASE_STAMPS), for stable_top_selection_amd.phase_report
+PHASES_LIB_PATH = os.path.join(PKG, "libdcptopk_phases.so")
+PHASE_FLAGS = ["-DDCPTOPK_PHASE_STAMPS=1"]
 # per-kernel register, scratch, occupancy and LDS figures of the last build,
 # from the compiler's resource-usage remarks
 RESOURCES_PATH = os.path.join(PKG, "libdcptopk.kernels.tsv")
@@ -111,13 +115,15 @@ def build(verbose: bool = False, extra_flags: list[str] | None = None, out: str 
 
 
 def build_all(verbose: bool = False) -> list[str]:
-    """Both libraries (product and race-stress test build), compiled concurrently."""
+    """The three libraries (product, race-stress test build, phase-stamp
+    build), compiled concurrently."""
     from concurrent.futures import ThreadPoolExecutor
 
-    with ThreadPoolExecutor(max_workers=2) as pool:
+    with ThreadPoolExecutor(max_workers=3) as pool:
         main = pool.submit(build, verbose)
         stress = pool.submit(build, False, STRESS_FLAGS, STRESS_LIB_PATH)
-        return [main.result(), stress.result()]
+        phases = pool.submit(build, False, PHASE_FLAGS, PHASES_LIB_PATH)
+        return [main.result(), stress.result(), phases.result()]
 
 
 if __name__ == "__main__":

@@ -118,6 +118,35 @@ __device__ __forceinline__ void lds_barrier() {
   }
 }
 
+// Phase stamps, a diagnostic build (DCPTOPK_PHASE_STAMPS=1, a library of its
+// own): lane 0 of the first and of the last wave of each of the first
+// kStampRows workgroups records the shader clock (s_memtime) at each phase
+// boundary of the select kernel, with a vector store into phase_stamps, which
+// dcptopk_phase_stamps copies out.  In every other build stamp() is empty.
+#ifndef DCPTOPK_PHASE_STAMPS
+#define DCPTOPK_PHASE_STAMPS 0
+#endif
+#if DCPTOPK_PHASE_STAMPS
+constexpr int kStampRows = 1024;  // workgroups stamped
+constexpr int kStampSlots = 16;   // phase boundaries per wave
+__device__ unsigned long long phase_stamps[kStampRows * 2 * kStampSlots];
+#endif
+
+template <int BLOCK>
+__device__ __forceinline__ void stamp(int phase, int w, int lane) {
+#if DCPTOPK_PHASE_STAMPS
+  __builtin_amdgcn_sched_barrier(0);  // the stamp stays where it is written
+  const unsigned long long now = __builtin_amdgcn_s_memtime();
+  if (lane == 0 && (w == 0 || w == BLOCK / kWave - 1) && blockIdx.x < kStampRows)
+    phase_stamps[(blockIdx.x * 2 + (w != 0)) * kStampSlots + phase] = now;
+  __builtin_amdgcn_sched_barrier(0);
+#else
+  (void)phase;
+  (void)w;
+  (void)lane;
+#endif
+}
+
 __device__ __forceinline__ uint32_t lane_of(uint32_t x, int lane) {
   return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(x), lane));
 }
@@ -866,6 +895,7 @@ __global__ __launch_bounds__(BLOCK) void stable_topk_kernel(Source src, Sink sin
   const int64_t row = blockIdx.x;
   const int C = src.count(row);
   const typename Sink::Row dst = sink.bind(row, k);
+  stamp<BLOCK>(0, w, lane);  // start
 
   // Wave w reads positions [w*64*N, (w+1)*64*N), 64*VEC consecutive ones per
   // load.
@@ -914,6 +944,7 @@ __global__ __launch_bounds__(BLOCK) void stable_topk_kernel(Source src, Sink sin
   if (t < 4) lds.common[t] = (t & 1) ? ~0u : 0u;  // OR slots 0, AND slots ~0 (list_common_bits)
   lds_barrier();
   __builtin_amdgcn_sched_barrier(0);
+  stamp<BLOCK>(1, w, lane);  // loads issued, LDS cleared, first barrier
 
   // FULL: the row fills every slot (C == BLOCK*N); else the last are masked
   // out: item i is valid if its position, first + (i / VEC) * kChunk + i % VEC,
@@ -959,14 +990,17 @@ __global__ __launch_bounds__(BLOCK) void stable_topk_kernel(Source src, Sink sin
     if constexpr (!FULL) target = ok(i) ? target : spare;
     rank_in_bin[i] = lds_add(target);
   }
+  stamp<BLOCK>(2, w, lane);  // pass-0 atomics issued
   lds_barrier();
   // padding keys counted in pass 0, in total and in the words before this lane's
+  stamp<BLOCK>(3, w, lane);  // pass-0 barrier
   const uint4 pw0 = *reinterpret_cast<const uint4*>(lds.padcnt);
   const uint4 pw1 = *reinterpret_cast<const uint4*>(lds.padcnt + 4);
   const uint32_t pad_total = pw0.x + pw0.y + pw0.z + pw0.w + pw1.x + pw1.y + pw1.z + pw1.w;
   static_assert(kPadWords == 8, "two uint4 reads");
   Radix sk{0u, 0u, static_cast<uint32_t>(k), 0u};
   advance(sk, find_digit_pass0(lds.hist[0], sk.need, lane, kPadBin, pad_total), 21, 0x7FFu);
+  stamp<BLOCK>(4, w, lane);  // digit search
 
   const uint32_t m = sk.count;  // items in the threshold bin
   bool tie = false, dup = false;
@@ -1002,9 +1036,11 @@ __global__ __launch_bounds__(BLOCK) void stable_topk_kernel(Source src, Sink sin
     lds_barrier();
   }
   __builtin_amdgcn_sched_barrier(0);
+  stamp<BLOCK>(5, w, lane);  // list built
   if (m != sk.need && m <= kListCap) {
     // then list pass 0 counts the next 8 key bits
     const uint2* items = list_pass<BLOCK, 13, 8, false, true>(lds, 0, m, 0u, sk, t, lane);
+    stamp<BLOCK>(6, w, lane);  // first list pass
     int q = 1;
     bool same_ids_known = false, resolved = false;
     uint32_t uor = 0u, uand = 0u;
@@ -1142,6 +1178,7 @@ __global__ __launch_bounds__(BLOCK) void stable_topk_kernel(Source src, Sink sin
     }
   }
 
+  stamp<BLOCK>(7, w, lane);  // threshold resolved
   uint32_t duprank[N];
   if (dup) {
     uint32_t same[N];
@@ -1179,8 +1216,10 @@ __global__ __launch_bounds__(BLOCK) void stable_topk_kernel(Source src, Sink sin
   // the loop has no per-item branch) while the waves' counts are exchanged,
   // then writes its range with consecutive stores.  A wave with more selected
   // items than its area stores every item at its rank from the registers.
+  stamp<BLOCK>(8, w, lane);  // selection flags
   uint32_t rank[N];
   const uint32_t out_count = wave_rank<VEC, N>(sel, rank, lane);
+  stamp<BLOCK>(9, w, lane);  // ranks
   if (lane == 0) lds.segment[1][w] = out_count;
   const bool staged = out_count <= static_cast<uint32_t>(kStageCap);  // wave-uniform
   if (staged) {
@@ -1190,8 +1229,10 @@ __global__ __launch_bounds__(BLOCK) void stable_topk_kernel(Source src, Sink sin
       stage[w][slot] = make_uint2(bits[i], idv[i]);
     }
   }
+  stamp<BLOCK>(10, w, lane);  // staging writes
   lds_barrier();
   const uint32_t out_first = waves_before<BLOCK>(lds.segment[1], w);
+  stamp<BLOCK>(11, w, lane);  // count exchange
   if (staged) {
     // all reads first, then all stores; slots past out_count hold stale
     // values, and their stores are dropped (the reads stay inside the wave's
@@ -1209,6 +1250,7 @@ __global__ __launch_bounds__(BLOCK) void stable_topk_kernel(Source src, Sink sin
 #pragma unroll
     for (int i = 0; i < N; ++i) dst.store(sel[i] != 0u, out_first + rank[i], bits[i], idv[i]);
   }
+  stamp<BLOCK>(12, w, lane);  // stores issued
 }
 
 // ---------------------------------------------------------------------------
@@ -1690,3 +1732,22 @@ hipError_t launch_select_split(const dcp_topk_cand* cand, int32_t rows, int32_t 
 }
 
 }  // namespace dcptopk
+
+#if DCPTOPK_PHASE_STAMPS
+// Copies the phase stamps of the launches since the last call out, then
+// clears them (diagnostic build only; synchronous).  bytes <=
+// sizeof(phase_stamps); the stamps of workgroup b, wave slot s (0: first wave,
+// 1: last wave) are the 16 words from (b * 2 + s) * 16; a phase the kernel did
+// not pass reads 0.
+extern "C" __attribute__((visibility("default"))) int dcptopk_phase_stamps(void* host, size_t bytes) {
+  if (bytes > sizeof(dcptopk::phase_stamps)) return -1;
+  hipError_t e = hipDeviceSynchronize();
+  if (e == hipSuccess)
+    e = hipMemcpyFromSymbol(host, HIP_SYMBOL(dcptopk::phase_stamps), bytes, 0, hipMemcpyDeviceToHost);
+  void* addr = nullptr;
+  if (e == hipSuccess) e = hipGetSymbolAddress(&addr, HIP_SYMBOL(dcptopk::phase_stamps));
+  if (e == hipSuccess) e = hipMemset(addr, 0, sizeof(dcptopk::phase_stamps));
+  if (e == hipSuccess) e = hipDeviceSynchronize();
+  return static_cast<int>(e);
+}
+#endif

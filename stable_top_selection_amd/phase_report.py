@@ -1,0 +1,138 @@
+"""Phase timeline of the select kernel on one MI355X, from the phase-stamp
+build of the library (``libdcptopk_phases.so``, compiled by ``build_all``).
+
+In that build lane 0 of the first and of the last wave of every workgroup
+reads the shader clock (``s_memtime``) at each phase boundary of the select
+kernel.  This script runs ``dcp_topk_select`` on a workload, reads the stamps
+of every workgroup (one row each) and prints, per phase, the median over the
+rows of the time from the start of wave 0 to the phase's end in the last wave
+(the later of the two) and the median length of the phase, in shader-clock
+cycles.  ``cold`` samples read inputs that no launch has touched since a pass
+over more than twice the Infinity Cache plus L2; ``warm`` samples repeat the
+previous launch's input.
+
+    python -m stable_top_selection_amd.phase_report [--workload large|decode16|tie_heavy] [--samples 8]
+
+The stamps cost a few instructions per boundary, so the absolute times are
+slightly above the product build's; the product's timing is bench.py's.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import os
+import statistics
+import sys
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PHASES = ["loads issued, LDS cleared, first barrier", "pass-0 atomics issued", "pass-0 barrier", "digit search",
+          "list built", "first list pass", "threshold resolved", "selection flags", "ranks", "staging writes",
+          "count exchange", "stores issued"]
+SLOTS = 16  # stamps per wave in the library's array
+STAMP_ROWS = 1024
+POOL_BYTES = 2 * (256 + 32) * (1 << 20)
+
+
+def _timelines(st: np.ndarray, rows: int):
+    """Per row: (end of each phase, the later of the two stamped waves, from
+    wave 0's start; the last wave's lag behind the first at that boundary);
+    phases the row did not pass are None."""
+    st = st.reshape(STAMP_ROWS, 2, SLOTS)[:rows].astype(np.int64)
+    out = []
+    for r in range(rows):
+        t0 = st[r, 0, 0]
+        ends = []
+        for p in range(1, len(PHASES) + 1):
+            a, b = st[r, 0, p], st[r, 1, p]
+            ends.append(None if (a == 0 and b == 0) else (int(max(a, b) - t0), int(b - a)))
+        out.append(ends)
+    return out
+
+
+def _summarise(lines):
+    """Per phase: rows that passed it, and over them the median end, median
+    length (from the previous phase the row passed) and median lag of the
+    last wave behind the first."""
+    res = []
+    for p in range(len(PHASES)):
+        ends = [ln[p][0] for ln in lines if ln[p] is not None]
+        lags = [ln[p][1] for ln in lines if ln[p] is not None]
+        lens = []
+        for ln in lines:
+            if ln[p] is None:
+                continue
+            prev = next((ln[q][0] for q in range(p - 1, -1, -1) if ln[q] is not None), 0)
+            lens.append(ln[p][0] - prev)
+        med = lambda x: statistics.median(x) if x else None  # noqa: E731
+        res.append((len(ends), med(ends), med(lens), med(lags)))
+    return res
+
+
+def main() -> None:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--workload", default="large", choices=["large", "decode16", "tie_heavy"])
+    ap.add_argument("--samples", type=int, default=8, help="launches stamped per mode")
+    args = ap.parse_args()
+
+    import torch
+
+    from stable_top_selection_amd import binding as B
+    from stable_top_selection_amd import build as BLD
+    from stable_top_selection_amd import workloads as W
+
+    lib = B.open_library(BLD.PHASES_LIB_PATH)
+    lib.dcptopk_phase_stamps.argtypes = [ctypes.c_void_p, ctypes.c_size_t]
+    lib.dcptopk_phase_stamps.restype = ctypes.c_int
+    g = {"large": W.large, "decode16": lambda: W.decode(16), "tie_heavy": W.tie_heavy}[args.workload]()
+    if g.rows > STAMP_ROWS:
+        raise SystemExit(f"at most {STAMP_ROWS} rows are stamped")
+    dev = torch.device("cuda:0")
+    inter = torch.from_numpy(g.interleaved()).to(dev)
+    per = inter.numel() * 4
+    n = max(args.samples + 1, -(-POOL_BYTES // per))
+    pool = [inter.clone() for _ in range(n)]
+    out = torch.empty((g.rows, g.k, 2), dtype=torch.int32, device=dev)
+    stamps = np.zeros(STAMP_ROWS * 2 * SLOTS, dtype=np.uint64)
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def launch(buf):
+        st = lib.dcp_topk_select(ctypes.c_void_p(buf.data_ptr()), g.rows, g.num_cand, g.k,
+                                 ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(stream))
+        if st != 0:
+            raise RuntimeError(f"dcp_topk_select: {B.status_string(st)}")
+
+    def read():
+        e = lib.dcptopk_phase_stamps(ctypes.c_void_p(stamps.ctypes.data), stamps.nbytes)
+        if e != 0:
+            raise RuntimeError(f"dcptopk_phase_stamps: {e}")
+        return _timelines(stamps, g.rows)
+
+    # the pool's buffers were written in order, so the earliest ones have left
+    # the caches by the time the last is written: cold samples take those
+    torch.cuda.synchronize()
+    read()  # clear
+    cold, warm = [], []
+    for s in range(args.samples):
+        launch(pool[s])
+        cold += read()
+        launch(pool[s])
+        warm += read()
+    print(f"workload {g.name}: {g.rows} rows x {g.num_cand} candidates, k {g.k}; "
+          f"{args.samples} launches per mode, medians over rows x launches, shader-clock cycles from wave 0's start")
+    print()
+    print("| Phase (end, later of the first and last wave) | Rows x launches passing | Cold: end | Cold: length | "
+          "Cold: last wave behind first | Warm: end | Warm: length |")
+    print("|---|---|---|---|---|---|---|")
+    for name, c, w in zip(PHASES, _summarise(cold), _summarise(warm)):
+        fmt = lambda x: "-" if x is None else f"{x:,.0f}"  # noqa: E731
+        print(f"| {name} | {c[0]} / {len(cold)} | {fmt(c[1])} | {fmt(c[2])} | {fmt(c[3])} | {fmt(w[1])} | "
+              f"{fmt(w[2])} |")
+
+
+if __name__ == "__main__":
+    main()
