@@ -1194,13 +1194,15 @@ __global__ __launch_bounds__(BLOCK) void stable_topk_kernel(Source src, Sink sin
     for (int i = 0; i < N; ++i) sel[i] = (ok(i) && key[i] >= sk.prefix) ? 1u : 0u;
   } else if (!dup) {
     // the tied items (key == threshold) are taken by complemented id; the id
-    // passes leave ik.prefix zero below ik.mask, so u >= prefix is the test
+    // passes leave ik.prefix zero below ik.mask, so the test is (key, ~id) >=
+    // (threshold key, ik.prefix), one 64-bit compare instead of three
+    // (tie-heavy 16 rows 8.08 -> 7.83 us, short-context 7.27 -> 7.12)
+    const uint64_t th = (static_cast<uint64_t>(sk.prefix) << 32) | ik.prefix;
 #pragma unroll
-    for (int i = 0; i < N; ++i) {
-      const uint32_t u = ~idv[i];
-      sel[i] = (ok(i) && (key[i] > sk.prefix || (key[i] == sk.prefix && u >= ik.prefix))) ? 1u : 0u;
-    }
+    for (int i = 0; i < N; ++i)
+      sel[i] = (ok(i) && ((static_cast<uint64_t>(key[i]) << 32) | ~idv[i]) >= th) ? 1u : 0u;
   } else {
+    // full duplicates of the threshold pair: the first ik.need by position
 #pragma unroll
     for (int i = 0; i < N; ++i) {
       const uint32_t u = ~idv[i];
