@@ -115,3 +115,33 @@ def test_grid_past_residency_is_unsupported():
     want_s, want_i = O.select(g.scores[:2], g.ids[:2], g.k)
     o = out[:2].cpu().numpy()
     assert np.array_equal(o[..., 0].view(np.uint32), want_s.view(np.uint32)) and np.array_equal(o[..., 1], want_i)
+
+
+def test_graph_replay_with_changing_inputs():
+    """The cooperative launch captured in a HIP graph: three replays over new
+    inputs copied into the captured buffer, with eager work in between; every
+    replay matches the oracle and leaves the counters at zero."""
+    rows, c, k, parts = 8, 8192, 2048, 4
+    cand = torch.zeros((rows, c, 2), dtype=torch.int32, device=DEV)
+    out = torch.empty((rows, k, 2), dtype=torch.int32, device=DEV)
+    ws = B.select_split_workspace(rows, c, parts, DEV)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        B.select_split(cand, k, parts, workspace=ws, out=out)  # first launch outside capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        B.select_split(cand, k, parts, workspace=ws, out=out)
+    for seed in (51, 52, 53):
+        g = W.random_gathered(rows, c, k, seed=seed, dist="levels" if seed % 2 else "normal")
+        print(f"[split] graph replay seed {seed}", flush=True)
+        cand.copy_(to_dev(g.interleaved()))
+        B.select(cand, 16)  # eager work between replays
+        graph.replay()
+        torch.cuda.synchronize()
+        o = out.cpu().numpy()
+        want_s, want_i = O.select(g.scores, g.ids, k)
+        assert np.array_equal(o[..., 0].view(np.uint32), want_s.view(np.uint32)) and np.array_equal(o[..., 1], want_i)
+        assert not ws[:rows * 16].view(torch.int32).cpu().numpy().any()
