@@ -248,9 +248,14 @@ def bench_eager(run, g, steps, trials):
     return statistics.median(res)
 
 
+PREFILL_REPEATS = 5  # whole merges (or pack / select passes) per graph replay
+
+
 def bench_prefill(run, trials):
-    """Whole chunked merge at T = 8192 (8 chunks of 1024 rows) in one graph, and
-    the select launches of the same chunks on their own."""
+    """Whole chunked merge at T = 8192 (8 chunks of 1024 rows), PREFILL_REPEATS
+    merges per graph replay so that the replay's own start-up is spread as in
+    the select timing, and the select and pack launches of the same chunks on
+    their own (the same number of passes per replay)."""
     import ctypes
 
     import numpy as np
@@ -280,8 +285,8 @@ def bench_prefill(run, trials):
         if st != 0:
             raise RuntimeError(run.B.status_string(st))
 
-    graph = run.graph_of([merge])
-    ms = run.time_graph(graph, trials)
+    graph = run.graph_of([merge] * PREFILL_REPEATS)
+    ms = [m / PREFILL_REPEATS for m in run.time_graph(graph, trials)]
     # sampled rows against the oracle (the oracle on all 8192 rows takes ~10 s)
     rows = np.unique(np.concatenate([np.arange(0, T, 97), [1023, 1024, 4095, 4096, T - 1]]))
     want_s, want_i = oracle.merge(sh.scores[:, rows], sh.local_idx[:, rows], sh.row_starts[:, rows], sh.rank_offsets, k)
@@ -295,8 +300,8 @@ def bench_prefill(run, trials):
     chunk_outs = [out[c0:c0 + 1024] for c0 in range(0, T, 1024)]
     sel = [lambda spp, o_=o_: run.select(gathered.data_ptr(), 1024, dcp * lk, k, o_.data_ptr(), spp)
            for o_ in chunk_outs]
-    g2 = run.graph_of(sel)
-    ms_sel = run.time_graph(g2, trials)
+    g2 = run.graph_of(sel * PREFILL_REPEATS)
+    ms_sel = [m / PREFILL_REPEATS for m in run.time_graph(g2, trials)]
     # pack alone: dcp_topk_pack of every rank of every chunk into the
     # workspace (one rank per launch; the chunked driver packs all ranks of a
     # chunk in one launch of the same kernel)
@@ -312,8 +317,8 @@ def bench_prefill(run, trials):
                 raise RuntimeError(run.B.status_string(st))
         return f
 
-    g3 = run.graph_of([pack_launch(c0, r) for c0 in range(0, T, 1024) for r in range(dcp)])
-    ms_pack = run.time_graph(g3, trials)
+    g3 = run.graph_of([pack_launch(c0, r) for c0 in range(0, T, 1024) for r in range(dcp)] * PREFILL_REPEATS)
+    ms_pack = [m / PREFILL_REPEATS for m in run.time_graph(g3, trials)]
     merge_ms = statistics.median(ms)
     sel_ms = statistics.median(ms_sel)
     pack_ms = statistics.median(ms_pack)
@@ -322,6 +327,7 @@ def bench_prefill(run, trials):
     pack_bytes = T * dcp * lk * (4 + 4 + 8) + dcp * T * 4
     gb = lambda b, t_ms: b / (t_ms * 1e-3) / 1e9  # noqa: E731
     return {"workload": f"prefill chunked: T={T}, DCP {dcp} x local K {lk}, K {k}, 1024-row chunks",
+            "merges_per_replay": PREFILL_REPEATS,
             "merge_ms": round(merge_ms, 4), "merge_trials_ms": [round(x, 4) for x in ms],
             "merge_GBps": round(gb(sel_bytes + pack_bytes, merge_ms), 1),
             "merge_candidates_per_s": round(T * dcp * lk / (merge_ms * 1e-3)),
@@ -414,8 +420,8 @@ def bench_fused(run, steps, warmup, trials):
         if st != 0:
             raise RuntimeError(run.B.status_string(st))
 
-    graph = run.graph_of([fused])
-    ms = statistics.median(run.time_graph(graph, trials))
+    graph = run.graph_of([fused] * PREFILL_REPEATS)
+    ms = statistics.median([m / PREFILL_REPEATS for m in run.time_graph(graph, trials)])
     rows = np.unique(np.concatenate([np.arange(0, T, 97), [1023, 1024, 4095, 4096, T - 1]]))
     want_s, want_i = oracle.merge(sh.scores[:, rows], sh.local_idx[:, rows], sh.row_starts[:, rows],
                                   sh.rank_offsets, k)
@@ -423,7 +429,8 @@ def bench_fused(run, steps, warmup, trials):
     if not (np.array_equal(o[..., 0].view(np.uint32), want_s.view(np.uint32)) and np.array_equal(o[..., 1], want_i)):
         raise AssertionError("fused prefill merge differs from the oracle on sampled rows")
     pre_bytes = T * dcp * lk * 8 + T * k * 8 + dcp * T * 4
-    res["prefill_one_launch"] = {"workload": f"prefill: T={T}, DCP {dcp} x local K {lk}, K {k}, one launch",
+    res["prefill_one_launch"] = {"workload": f"prefill: T={T}, DCP {dcp} x local K {lk}, K {k}, one launch "
+                                             f"({PREFILL_REPEATS} per graph replay)",
                                  "ms": round(ms, 4), "GBps": round(pre_bytes / (ms * 1e-3) / 1e9, 1),
                                  "rows_checked": int(len(rows))}
     return res
