@@ -621,7 +621,8 @@ __device__ __forceinline__ void position_rank(const uint32_t (&flag)[N], uint32_
 // first = w*64*N + VEC*lane.  count(row) is the row's candidate count C (at
 // most the launch's num_cand); the values at positions at or past C are
 // ignored.  load() only issues the reads (into bits/idv and, for per-chunk
-// wave-uniform values, aux); finish<VEC>(v, ...) turns what arrived for chunk
+// values the same across the wave, two words per chunk of aux);
+// finish<VEC>(v, ...) turns what arrived for chunk
 // v into (score bits, id).  The kernel finishes each chunk just before it
 // first uses it, after its first barrier, so the loads stay in flight while
 // it clears LDS and the work on early chunks overlaps later chunks' arrival.
@@ -678,11 +679,13 @@ struct GatheredSource {
 // id is local index + row start + rank offset with two's-complement wrap, and
 // a negative local index is the padding candidate (vLLM PR #59367, Purpose).
 // local_k is a multiple of 64*VEC, so a chunk never straddles two ranks and a
-// chunk's rank is wave-uniform.  A wave reads its chunks' rank-table entries
-// and then their row starts (scalar loads) before its first data load, so the
-// id bases are back by the time the first chunk arrives (measured against
-// reading the row starts after the last data load: 256 rows 8.14 -> 8.02 us,
-// 8192 rows 134.5 -> 132.2 us).
+// chunk's rank is wave-uniform.  A wave reads every chunk's rank-table entry
+// in one round of scalar loads, then the chunks' row starts as vector loads
+// and then the data, all without a wait in between: a chunk's id base
+// (row start in aux[2v], rank offset in aux[2v+1]) is back when its data is.
+// (Against one round of scalar loads per chunk, each waiting for its row start
+// before the next: 256 rows 8.13 -> 8.09 us, 8192 rows in one launch 125.5 ->
+// 122.8 us, in one process on one box.)
 struct RankSource {
   static constexpr bool kChunkLoads = false;  // a wave's loads go out together (see load)
   FusedRanks ranks;
@@ -728,9 +731,20 @@ struct RankSource {
       rp[v] = pr.row_starts;
       off[v] = static_cast<uint32_t>(pr.rank_offset);
     }
-    // (wave-uniform: scalar registers)
+    __builtin_amdgcn_sched_barrier(0);  // every chunk's rank entry in one round of scalar loads
+    // the chunks' row starts as vector loads, ahead of the data loads: the
+    // data loads issue without waiting for them, the first barrier (which
+    // waits for scalar loads) does not either, and waiting for a chunk's data
+    // covers its row start (loads return in order)
 #pragma unroll
-    for (int v = 0; v < NV; ++v) aux[v] = uniform(static_cast<uint32_t>(rp[v][row]) + off[v]);
+    for (int v = 0; v < NV; ++v) {
+      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<int32_t*>(rp[v]), 0, static_cast<int>(row + 1) * static_cast<int>(sizeof(int32_t)),
+          static_cast<int>(kBufferWord3));
+      aux[2 * v] = static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b32(rs, static_cast<int>(row) * 4, 0, 0));
+      aux[2 * v + 1] = off[v];
+    }
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int v = 0; v < NV; ++v) {
       const int64_t at = row * local_k + j0[v] + lane_off;
@@ -765,7 +779,7 @@ struct RankSource {
   // bits/idv hold score bits and local indices, aux the chunks' id bases
   template <int VEC>
   __device__ __forceinline__ void finish(int v, const uint32_t* aux, uint32_t* bits, uint32_t* idv) const {
-    const uint32_t base = aux[v];
+    const uint32_t base = aux[2 * v] + aux[2 * v + 1];
 #pragma unroll
     for (int j = 0; j < VEC; ++j) {
       const bool invalid = static_cast<int32_t>(idv[v * VEC + j]) < 0;
@@ -900,7 +914,7 @@ __global__ __launch_bounds__(BLOCK) void stable_topk_kernel(Source src, Sink sin
   // Wave w reads positions [w*64*N, (w+1)*64*N), 64*VEC consecutive ones per
   // load.
   const int first = w * kWave * N + VEC * lane;  // this thread's position in chunk 0
-  uint32_t bits[N], idv[N], aux[NV];
+  uint32_t bits[N], idv[N], aux[2 * NV];
 
   // k >= C: every candidate is selected, in place, then padding (a branch
   // of its own from the start, so that none of its code is shared with, and

@@ -11,7 +11,11 @@ cycles.  ``cold`` samples read inputs that no launch has touched since a pass
 over more than twice the Infinity Cache plus L2; ``warm`` samples repeat the
 previous launch's input.
 
-    python -m stable_top_selection_amd.phase_report [--workload large|decode16|tie_heavy] [--samples 8]
+    python -m stable_top_selection_amd.phase_report [--workload large|decode16|tie_heavy|fused] [--samples 8]
+
+``fused`` runs the fused merge (dcp_topk_merge_fused) on the large shape
+(256 rows, DCP 4 x local K 2048), whose kernel reads every rank's local
+arrays in place; the others run dcp_topk_select on a gathered buffer.
 
 The stamps cost a few instructions per boundary, so the absolute times are
 slightly above the product build's; the product's timing is bench.py's.
@@ -75,8 +79,9 @@ def _summarise(lines):
 
 def main() -> None:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
-    ap.add_argument("--workload", default="large", choices=["large", "decode16", "tie_heavy"])
+    ap.add_argument("--workload", default="large", choices=["large", "decode16", "tie_heavy", "fused"])
     ap.add_argument("--samples", type=int, default=8, help="launches stamped per mode")
+    ap.add_argument("--lib", default=None, help="a phase-stamp build of the library (default: the package's)")
     args = ap.parse_args()
 
     import torch
@@ -85,32 +90,54 @@ def main() -> None:
     from stable_top_selection_amd import build as BLD
     from stable_top_selection_amd import workloads as W
 
-    lib = B.open_library(BLD.PHASES_LIB_PATH)
+    lib = B.open_library(args.lib or BLD.PHASES_LIB_PATH)
     lib.dcptopk_phase_stamps.argtypes = [ctypes.c_void_p, ctypes.c_size_t]
     lib.dcptopk_phase_stamps.restype = ctypes.c_int
-    g = {"large": W.large, "decode16": lambda: W.decode(16), "tie_heavy": W.tie_heavy}[args.workload]()
-    if g.rows > STAMP_ROWS:
-        raise SystemExit(f"at most {STAMP_ROWS} rows are stamped")
     dev = torch.device("cuda:0")
-    inter = torch.from_numpy(g.interleaved()).to(dev)
-    per = inter.numel() * 4
-    n = max(args.samples + 1, -(-POOL_BYTES // per))
-    pool = [inter.clone() for _ in range(n)]
-    out = torch.empty((g.rows, g.k, 2), dtype=torch.int32, device=dev)
-    stamps = np.zeros(STAMP_ROWS * 2 * SLOTS, dtype=np.uint64)
     stream = torch.cuda.current_stream().cuda_stream
+    if args.workload == "fused":
+        sh = W.fused()
+        rows, k, name, num_cand = sh.rows, sh.k, sh.name, sh.dcp * sh.local_k
+        to = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)  # noqa: E731
+        per = sh.dcp * sh.rows * sh.local_k * 8
+        n = max(args.samples + 1, -(-POOL_BYTES // per))
+        # a pool of copies of the ranks' arrays: each entry holds the device
+        # tensors (kept alive here) and the host arrays of their pointers
+        pool = []
+        for _ in range(n):
+            arrays = ([to(sh.scores[r]) for r in range(sh.dcp)], [to(sh.local_idx[r]) for r in range(sh.dcp)],
+                      [to(sh.row_starts[r]) for r in range(sh.dcp)])
+            pool.append((arrays, B._RankArrays(*arrays, [int(x) for x in sh.rank_offsets])))
+        out = torch.empty((rows, k, 2), dtype=torch.int32, device=dev)
 
-    def launch(buf):
-        st = lib.dcp_topk_select(ctypes.c_void_p(buf.data_ptr()), g.rows, g.num_cand, g.k,
-                                 ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(stream))
-        if st != 0:
-            raise RuntimeError(f"dcp_topk_select: {B.status_string(st)}")
+        def launch(entry):
+            st = lib.dcp_topk_merge_fused(*entry[1].args(), sh.dcp, rows, sh.local_k, k,
+                                          ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(stream))
+            if st != 0:
+                raise RuntimeError(f"dcp_topk_merge_fused: {B.status_string(st)}")
+    else:
+        g = {"large": W.large, "decode16": lambda: W.decode(16), "tie_heavy": W.tie_heavy}[args.workload]()
+        rows, k, name, num_cand = g.rows, g.k, g.name, g.num_cand
+        inter = torch.from_numpy(g.interleaved()).to(dev)
+        per = inter.numel() * 4
+        n = max(args.samples + 1, -(-POOL_BYTES // per))
+        pool = [inter.clone() for _ in range(n)]
+        out = torch.empty((rows, k, 2), dtype=torch.int32, device=dev)
+
+        def launch(buf):
+            st = lib.dcp_topk_select(ctypes.c_void_p(buf.data_ptr()), rows, num_cand, k,
+                                     ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(stream))
+            if st != 0:
+                raise RuntimeError(f"dcp_topk_select: {B.status_string(st)}")
+    if rows > STAMP_ROWS:
+        raise SystemExit(f"at most {STAMP_ROWS} rows are stamped")
+    stamps = np.zeros(STAMP_ROWS * 2 * SLOTS, dtype=np.uint64)
 
     def read():
         e = lib.dcptopk_phase_stamps(ctypes.c_void_p(stamps.ctypes.data), stamps.nbytes)
         if e != 0:
             raise RuntimeError(f"dcptopk_phase_stamps: {e}")
-        return _timelines(stamps, g.rows)
+        return _timelines(stamps, rows)
 
     # the pool's buffers were written in order, so the earliest ones have left
     # the caches by the time the last is written: cold samples take those
@@ -122,7 +149,7 @@ def main() -> None:
         cold += read()
         launch(pool[s])
         warm += read()
-    print(f"workload {g.name}: {g.rows} rows x {g.num_cand} candidates, k {g.k}; "
+    print(f"workload {name}: {rows} rows x {num_cand} candidates, k {k}; "
           f"{args.samples} launches per mode, medians over rows x launches, shader-clock cycles from wave 0's start")
     print()
     print("| Phase (end, later of the first and last wave) | Rows x launches passing | Cold: end | Cold: length | "
