@@ -1365,7 +1365,8 @@ __global__ __launch_bounds__(BLOCK) void split_select_kernel(const dcp_topk_cand
   const int64_t row = blockIdx.x / parts;
   const int s = static_cast<int>(blockIdx.x % parts);
   const int start = s * slice_len;  // the slice's first position in the row
-  const int len = num_cand - start < slice_len ? num_cand - start : slice_len;  // its candidates (>= 0)
+  // its candidates: none when the slice starts at or past the row's end
+  const int len = num_cand <= start ? 0 : (num_cand - start < slice_len ? num_cand - start : slice_len);
   uint32_t* ctrl = ws.ctrl + row * 4;
   uint32_t* hist_g = ws.hist + row * parts * kSplitHist;
   uint2* list = ws.list + row * num_cand;
@@ -1381,7 +1382,7 @@ __global__ __launch_bounds__(BLOCK) void split_select_kernel(const dcp_topk_cand
   {
     const __amdgpu_buffer_rsrc_t src = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<dcp_topk_cand*>(cand + row * num_cand + start), 0,
-        (len > 0 ? len : 0) * static_cast<int>(sizeof(dcp_topk_cand)), static_cast<int>(kBufferWord3));
+        len * static_cast<int>(sizeof(dcp_topk_cand)), static_cast<int>(kBufferWord3));
     const int voff = first * static_cast<int>(sizeof(dcp_topk_cand));
 #pragma unroll
     for (int v = 0; v < NV; ++v) {
