@@ -59,8 +59,8 @@ def parse_args():
                    help="select launches per timed trial (at least 200 are timed, a whole number of pool passes)")
     p.add_argument("--warmup", type=int, default=20, help="untimed launches before timing")
     p.add_argument("--trials", type=int, default=7)
-    p.add_argument("--configs", default="large,large_warm,large_eager,decode,split,tie_heavy,short_context,prefill,fused,local",
-                   help="comma list of large_warm, large_eager, decode, split, tie_heavy, short_context, prefill, fused, "
+    p.add_argument("--configs", default="large,large_warm,large_eager,decode,pages,split,tie_heavy,short_context,prefill,fused,local",
+                   help="comma list of large_warm, large_eager, decode, pages, split, tie_heavy, short_context, prefill, fused, "
                         "local; the cold large headline always runs (--configs large runs it alone, as profiled)")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU oracle work to time")
@@ -223,6 +223,36 @@ def bench_split(run, steps, warmup, trials, decode=None):
         out[f"rows{rows}"] = line
         log(f"[split rows={rows}] {line}")
     torch.cuda.empty_cache()
+    return out
+
+
+# The pages' selector table (PR #47348, Benchmarks: median us of 7 x 200
+# launches; hardware, K and score distributions not stated): (rows, candidates,
+# distribution) -> us of the PR's selector.  Context only.
+PAGES_SELECTOR_US = [((16, 4096, "random"), 6.721), ((16, 8192, "random"), 11.478),
+                     ((16, 16384, "random"), 20.684), ((64, 8192, "random"), 11.696),
+                     ((256, 8192, "random"), 15.459), ((16, 8192, "tie-heavy"), 20.396)]
+
+
+def bench_pages_table(run, steps, warmup, trials):
+    """Every case of the pages' selector table with this select, cold pools,
+    K 2048: "random" rows of 8192 are the decode workload (N(0,1)) at 16 and
+    64 rows and the large workload (U(-10,10)) at 256; 4096 and 16384 use
+    N(0,1) scores with distinct ids; "tie-heavy" is the tie-heavy workload."""
+    from stable_top_selection_amd import workloads as W
+    out = []
+    for (rows, c, dist), pages_us in PAGES_SELECTOR_US:
+        if dist == "tie-heavy":
+            g = W.tie_heavy(rows=rows)
+        elif c == 8192:
+            g = W.large() if rows == 256 else W.decode(rows)
+        else:
+            g = W.random_gathered(rows, c, 2048, seed=4700 + c, dist="normal")
+        res = bench_select(run, g, steps, warmup, trials, cold=True)
+        us = res["us_per_launch"]
+        out.append({"rows": rows, "candidates": c, "distribution": dist, "workload": g.name, "k": g.k,
+                    "cold_us": round(us, 3), "pages_us": pages_us, "pages_over_this": round(pages_us / us, 2)})
+        log(f"[pages table] rows={rows} C={c} {dist}: {us:.3f} us (pages {pages_us} us)")
     return out
 
 
@@ -666,6 +696,8 @@ def main():
                                     "cold_frac_of_peak": cold["frac_of_peak"]}
             log(f"[decode rows={rows}] cold {cold['us_per_launch']:.3f} us, warm {hot['us_per_launch']:.3f} us")
         extra["decode_latency_us"] = sweep
+    if "pages" in configs:
+        extra["pages_selector_table"] = bench_pages_table(run, args.steps, args.warmup, args.trials)
     if "split" in configs:
         extra["split_rows_latency_us"] = bench_split(run, args.steps, args.warmup, args.trials,
                                                      extra.get("decode_latency_us"))
