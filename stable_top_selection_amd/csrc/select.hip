@@ -59,6 +59,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "internal.h"
 
 namespace dcptopk {
@@ -1637,8 +1639,9 @@ hipError_t launch(const Source& src, const Sink& sink, bool uniform_rows, int32_
   return hipLaunchKernel(fn, dim3(rows), dim3(BLOCK), args, 0, stream);
 }
 
-// 256 threads up to 2048 candidates, 512 above; the smallest item count per
-// thread that covers the row.  VEC 1 and 2:
+// 256 threads up to 2048 candidates, 512 above (1024 for the rows past 8192
+// noted below); the smallest item count per thread that covers the row.
+// VEC 1 and 2:
 template <int VEC, class Source, class Sink>
 hipError_t launch_sized_narrow(const Source& src, const Sink& sink, bool u, int32_t rows, int32_t num_cand,
                                int32_t k, hipStream_t stream) {
@@ -1649,6 +1652,13 @@ hipError_t launch_sized_narrow(const Source& src, const Sink& sink, bool u, int3
   if (num_cand <= 2048) return launch<256, VEC, 8>(src, sink, u, rows, num_cand, k, stream);
   if (num_cand <= 4096) return launch<512, VEC, 8>(src, sink, u, rows, num_cand, k, stream);
   if (num_cand <= 8192) return launch<512, VEC, 16>(src, sink, u, rows, num_cand, k, stream);
+  if constexpr (std::is_same<Source, GatheredSource>::value) {
+    // rows of 8192 to 16384: a full 16384-candidate row keeps 512 threads x
+    // 32 items; a partial row takes 1024 threads x 16 items, at 4 waves per
+    // SIMD where the partial-row 32-item kernel has 2 (2048 rows x 12000,
+    // k 3000: 83.5 -> 77.4 us; 16 rows x 16384 at 1024 x 16: 8.20 -> 8.88 us)
+    if (!(u && num_cand == 512 * 32)) return launch<1024, VEC, 16>(src, sink, u, rows, num_cand, k, stream);
+  }
   return launch<512, VEC, 32>(src, sink, u, rows, num_cand, k, stream);
 }
 
@@ -1662,10 +1672,11 @@ hipError_t launch_sized(const Source& src, const Sink& sink, bool uniform_rows, 
     if (num_cand <= 2048) return launch<256, 4, 8>(src, sink, u, rows, num_cand, k, stream);
     if (num_cand <= 4096) return launch<512, 4, 8>(src, sink, u, rows, num_cand, k, stream);
     if (num_cand <= 8192) return launch<512, 4, 16>(src, sink, u, rows, num_cand, k, stream);
-    // 32 items per thread: two-item loads (any source that allows four-item
-    // loads allows two), because the four-item form of the partial-row kernel
-    // needs more than 256 VGPRs and spills
-    return launch<512, 2, 32>(src, sink, u, rows, num_cand, k, stream);
+    // more than 8192: 1024 threads x 16 items (4 waves per SIMD; 512 x 32
+    // has 2: fused merge 256 rows of DCP 8 x 2048 14.6 -> 12.6 us, 2048 rows
+    // of DCP 6 x 2048 101.3 -> 88.5 us; local top-K with per-row lengths,
+    // 64 x 16384 9.91 -> 8.85 us, 2048 x 12000 72.9 -> 61.0 us)
+    return launch<1024, 4, 16>(src, sink, u, rows, num_cand, k, stream);
   } else {
     return launch_sized_narrow<VEC>(src, sink, u, rows, num_cand, k, stream);
   }

@@ -73,3 +73,20 @@ def test_remark_parser():
             "a.hip:1:1: remark:     LDS Size [bytes/block]: 77680 [-Rpass-analysis=kernel-resource-usage]\n"
             "    1 | int x;\n")
     assert BLD.parse_resource_remarks(text) == {"kern": {"vgprs": 113, "waves_per_simd": 4, "lds_bytes": 77680}}
+
+
+def test_1024_thread_kernels_fit_the_simds():
+    """Rows of more than 8192 candidates (partial gathered rows, every fused
+    and dense row) run 1024 threads x 16 items: a workgroup of 16 waves needs
+    4 waves per SIMD (at most 128 VGPRs) to launch at all, and its LDS must fit
+    one CU."""
+    seen = set()
+    for name, block, vec, n, full, source, r in _select_kernels():
+        if block == 1024:
+            seen.add((source, vec, full))
+            assert n == 16, name
+            assert r["waves_per_simd"] >= 4, f"{name}: {r['vgprs']} VGPRs"
+            assert r["lds_bytes"] <= 160 * 1024, f"{name}: {r['lds_bytes']} B of LDS"
+    expected = {("GatheredSource", 1, False), ("GatheredSource", 2, False), ("RankSource", 4, False),
+                ("RankSource", 4, True), ("DenseSource", 4, False), ("DenseSource", 4, True)}
+    assert expected <= seen, sorted(expected - seen)
