@@ -11,7 +11,8 @@ what the barrier published, so a buffer reused without a barrier after its last
 read would give a wrong result.  Every case must still match the oracle bit
 for bit: the tie-heavy workload on 256 rows, the large workload, padding-heavy
 rows, the register passes (one shared key), full duplicates (the position
-rank), 32 items per thread, the fused merge and the local top-K.
+rank), 32 items per thread, 1024 threads x 16 items (rows past 8192
+candidates), the fused merge, the local top-K and the split-row select.
 """
 import numpy as np
 import pytest
@@ -60,6 +61,7 @@ def test_padding_heavy_rows():
     (4, 16384, 5000, "levels", {}),                                 # 32 items per thread
     (5, 2049, 1000, "levels", {}),
     (3, 1025, 1, "special", {}),
+    (3, 12000, 3000, "levels", {}),                                 # 1024 threads x 16 items (partial row)
 ])
 def test_ragged_and_degenerate(rows, c, k, dist, kw):
     _select(W.random_gathered(rows, c, k, seed=900 + c + k, dist=dist, **kw), f"{dist} {kw}")
@@ -129,3 +131,15 @@ def test_split_rows(make, parts):
     gb, gi = gpu_select(g.scores, g.ids, g.k, split_parts=parts)
     os_, oi = O.select(g.scores, g.ids, g.k)
     assert np.array_equal(gb, os_.view(np.uint32)) and np.array_equal(gi, oi)
+
+
+def test_local_topk_long_rows():
+    """Rows of more than 8192 columns with per-row lengths: the 1024-thread
+    dense kernel."""
+    d = W.local(rows=8, num_cols=12288, k=2048, dist="levels", with_lengths=True)
+    print(f"[race stress] local top-K {d.name}", flush=True)
+    os_, oi = B.local_topk(to_dev(d.scores), d.k, lengths=to_dev(d.lengths))
+    torch.cuda.synchronize()
+    ws, wi = O.local_topk(d.scores, d.k, d.lengths)
+    assert np.array_equal(os_.cpu().numpy().view(np.uint32), ws.view(np.uint32))
+    assert np.array_equal(oi.cpu().numpy(), wi)
