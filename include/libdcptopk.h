@@ -151,8 +151,8 @@ DCP_TOPK_API int dcp_topk_select(const dcp_topk_cand* cand, int32_t rows, int32_
  * multiple of 256 bytes: rows * 16 bytes of counters, rows * parts * 8224
  * bytes of slice histograms, rows * num_cand * 8 bytes of threshold-bin list
  * entries and rows * num_cand * 4 bytes of their positions.  Returns 0 for
- * arguments outside rows >= 0, num_cand >= 0, 1 <= parts <=
- * DCP_TOPK_SPLIT_MAX_PARTS.
+ * arguments outside rows >= 0, 0 <= num_cand <= DCP_TOPK_MAX_CANDIDATES,
+ * 1 <= parts <= DCP_TOPK_SPLIT_MAX_PARTS.
  */
 DCP_TOPK_API size_t dcp_topk_select_split_workspace_bytes(int32_t rows, int32_t num_cand, int32_t parts);
 
@@ -197,7 +197,8 @@ DCP_TOPK_API int dcp_topk_select_split(const dcp_topk_cand* cand, int32_t rows, 
  * local_k * 8 bytes.  (PR #59367, Purpose, bounds the scratch of its
  * multi-GPU merge at (1 + 2 dcp) * 8 * 1024 * K bytes; on one GPU nothing is
  * exchanged, so only the buffer the selector reads remains.)  Returns 0 for
- * negative arguments.
+ * negative arguments and when the size does not fit in a size_t (such shapes
+ * exceed DCP_TOPK_MAX_CANDIDATES, which the merge rejects).
  */
 DCP_TOPK_API size_t dcp_topk_merge_workspace_bytes(int32_t rows, int32_t dcp, int32_t local_k);
 

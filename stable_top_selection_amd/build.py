@@ -25,6 +25,13 @@ STRESS_FLAGS = ["-DDCPTOPK_RACE_STRESS=1"]
 # boundaries (DCPTOPK_PHASE_STAMPS), for stable_top_selection_amd.phase_report
 PHASES_LIB_PATH = os.path.join(PKG, "libdcptopk_phases.so")
 PHASE_FLAGS = ["-DDCPTOPK_PHASE_STAMPS=1"]
+# the same library with its host code (the C ABI's checks and launch set-up)
+# built with AddressSanitizer and UndefinedBehaviorSanitizer; the device code
+# is the product's.  Only the CPU tests load it, in a process that preloads the
+# ASan runtime (tests/test_abi_sanitized_cpu.py).
+SANITIZED_LIB_PATH = os.path.join(PKG, "libdcptopk_host_sanitized.so")
+SANITIZE_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                  "-Xarch_host", "-fno-sanitize-recover=all", "-Xarch_host", "-fno-omit-frame-pointer"]
 # per-kernel register, scratch, occupancy and LDS figures of the last build,
 # from the compiler's resource-usage remarks
 RESOURCES_PATH = os.path.join(PKG, "libdcptopk.kernels.tsv")
@@ -115,15 +122,16 @@ def build(verbose: bool = False, extra_flags: list[str] | None = None, out: str 
 
 
 def build_all(verbose: bool = False) -> list[str]:
-    """The three libraries (product, race-stress test build, phase-stamp
-    build), compiled concurrently."""
+    """The four libraries (product, race-stress test build, phase-stamp build,
+    host-sanitized build), compiled concurrently."""
     from concurrent.futures import ThreadPoolExecutor
 
-    with ThreadPoolExecutor(max_workers=3) as pool:
+    with ThreadPoolExecutor(max_workers=4) as pool:
         main = pool.submit(build, verbose)
         stress = pool.submit(build, False, STRESS_FLAGS, STRESS_LIB_PATH)
         phases = pool.submit(build, False, PHASE_FLAGS, PHASES_LIB_PATH)
-        return [main.result(), stress.result(), phases.result()]
+        sanitized = pool.submit(build, False, SANITIZE_FLAGS, SANITIZED_LIB_PATH)
+        return [main.result(), stress.result(), phases.result(), sanitized.result()]
 
 
 if __name__ == "__main__":

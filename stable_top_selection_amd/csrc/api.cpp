@@ -176,7 +176,11 @@ const char* dcp_topk_status_string(int status) {
 size_t dcp_topk_merge_workspace_bytes(int32_t rows, int32_t dcp, int32_t local_k) {
   if (rows < 0 || dcp < 0 || local_k < 0) return 0;
   const int64_t chunk = rows < DCP_TOPK_MERGE_ROWS ? rows : DCP_TOPK_MERGE_ROWS;
-  return static_cast<size_t>(chunk) * static_cast<size_t>(dcp) * static_cast<size_t>(local_k) * kCandBytes;
+  // 1024 rows of up to 2^62 candidates can exceed size_t: such a shape has no
+  // valid size (and the merge rejects it as unsupported)
+  const unsigned __int128 b = static_cast<unsigned __int128>(chunk) * static_cast<uint64_t>(dcp) *
+                              static_cast<uint64_t>(local_k) * kCandBytes;
+  return b > SIZE_MAX ? 0 : static_cast<size_t>(b);
 }
 
 int dcp_topk_select(const dcp_topk_cand* cand, int32_t rows, int32_t num_cand, int32_t k, dcp_topk_cand* out,
@@ -187,7 +191,10 @@ int dcp_topk_select(const dcp_topk_cand* cand, int32_t rows, int32_t num_cand, i
 }
 
 size_t dcp_topk_select_split_workspace_bytes(int32_t rows, int32_t num_cand, int32_t parts) {
-  if (rows < 0 || num_cand < 0 || parts < 1 || parts > DCP_TOPK_SPLIT_MAX_PARTS) return 0;
+  // (num_cand <= DCP_TOPK_MAX_CANDIDATES also keeps the byte count far below
+  // the range of size_t)
+  if (rows < 0 || num_cand < 0 || num_cand > DCP_TOPK_MAX_CANDIDATES || parts < 1 || parts > DCP_TOPK_SPLIT_MAX_PARTS)
+    return 0;
   return dcptopk::split_layout(rows, num_cand, parts).bytes;
 }
 

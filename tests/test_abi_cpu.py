@@ -3,6 +3,7 @@ declares, and its host-side checks return the documented status codes without
 enqueueing anything (no GPU is touched: every call here fails validation, or
 has rows == 0, before any HIP call)."""
 import ctypes
+import os
 import subprocess
 
 import pytest
@@ -11,6 +12,11 @@ from oracle import stable_topk as O
 from stable_top_selection_amd import binding as B
 from stable_top_selection_amd.build import LIB_PATH, STRESS_LIB_PATH
 
+# the library under test: the product build, or another build of the same
+# sources named by DCPTOPK_ABI_TEST_LIB (test_abi_sanitized_cpu.py runs this
+# module on the host-sanitized build)
+ABI_LIB = os.environ.get("DCPTOPK_ABI_TEST_LIB", LIB_PATH)
+
 P = ctypes.c_void_p
 DEV_A = 0x7F0000000000  # fake, 256-byte aligned device addresses: never dereferenced
 DEV_B = 0x7F0010000000
@@ -18,7 +24,7 @@ DEV_B = 0x7F0010000000
 
 @pytest.fixture(scope="module")
 def lib():
-    return B.load_library()
+    return B.load_library() if ABI_LIB == LIB_PATH else B.open_library(ABI_LIB)
 
 
 def test_exports_every_header_function(lib):
@@ -29,7 +35,7 @@ def test_exports_every_header_function(lib):
                           "dcp_topk_select_split_workspace_bytes"}
     for n in names:
         assert hasattr(lib, n), n
-    exported = subprocess.run(["nm", "-D", "--defined-only", LIB_PATH], capture_output=True, text=True).stdout
+    exported = subprocess.run(["nm", "-D", "--defined-only", ABI_LIB], capture_output=True, text=True).stdout
     public = sorted(line.split()[-1] for line in exported.splitlines() if " T dcp_topk_" in line)
     assert public == names
 
@@ -47,13 +53,15 @@ def test_race_stress_build_exports_the_same_functions():
 
 
 def test_status_strings(lib):
-    assert B.status_string(0) == "ok"
-    assert "invalid" in B.status_string(-1)
-    assert "unsupported" in B.status_string(-2)
-    assert "workspace" in B.status_string(-3)
-    assert "HIP" in B.status_string(-4)
-    assert "static scratch" in B.status_string(-5)
-    assert B.status_string(99) == "unknown status"
+    st = lambda code: lib.dcp_topk_status_string(code).decode()  # noqa: E731
+    assert st(0) == "ok"
+    assert "invalid" in st(-1)
+    assert "unsupported" in st(-2)
+    assert "workspace" in st(-3)
+    assert "HIP" in st(-4)
+    assert "static scratch" in st(-5)
+    assert st(99) == "unknown status"
+    assert B.status_string(-1) == st(-1)
 
 
 @pytest.mark.parametrize("rows,dcp,local_k", [(0, 4, 2048), (1, 4, 2048), (1024, 4, 2048), (1025, 4, 2048),
@@ -61,6 +69,14 @@ def test_status_strings(lib):
 def test_workspace_bytes_match_oracle(lib, rows, dcp, local_k):
     want = O.merge_workspace_bytes(rows, dcp, local_k) if rows >= 0 else 0
     assert lib.dcp_topk_merge_workspace_bytes(rows, dcp, local_k) == want
+
+
+def test_workspace_bytes_that_do_not_fit_a_size_t(lib):
+    """1024 rows of 2^62 candidates need 2^75 bytes: no size, so 0 (the merge
+    rejects such a shape as unsupported before it looks at the workspace)."""
+    big = 2**31 - 1
+    assert lib.dcp_topk_merge_workspace_bytes(1024, big, big) == 0
+    assert lib.dcp_topk_merge_workspace_bytes(big, 16, big) == O.merge_workspace_bytes(big, 16, big)
 
 
 def test_select_argument_checks(lib):
@@ -190,6 +206,7 @@ def test_split_workspace_bytes(lib, rows, num_cand, parts):
 def test_split_workspace_bytes_rejects_bad_arguments(lib):
     f = lib.dcp_topk_select_split_workspace_bytes
     assert f(-1, 8192, 4) == 0 and f(1, -1, 4) == 0 and f(1, 8192, 0) == 0 and f(1, 8192, 9) == 0
+    assert f(1, 16385, 4) == 0 and f(2**31 - 1, 2**31 - 1, 8) == 0  # past DCP_TOPK_MAX_CANDIDATES
 
 
 def test_select_split_argument_checks(lib):
