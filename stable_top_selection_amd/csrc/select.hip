@@ -33,7 +33,8 @@
 //      finds the bin d0 holding the K-th best key (two-level suffix scan: DPP
 //      wave scans and ballots).
 //   3. The items of bin d0 (a few percent of the row for smooth scores) write
-//      themselves into an LDS list at their rank.  The remaining 21 key bits
+//      themselves (score bits, id) into an LDS list at their rank; the list
+//      passes turn the bits back into keys.  The remaining 21 key bits
 //      are radix-selected over the list only (digits of 8, 8, 5 bits, small
 //      histograms), stopping as soon as the chosen bin holds exactly the items
 //      still needed.  Each list pass also keeps the first 8 items of every
@@ -318,7 +319,7 @@ struct alignas(16) SelectLds {
   uint32_t hist[3][kBins];         // pass 0 (hist[0]) and the register passes, rotating
   uint32_t small[3][kSmallBins];   // list passes, rotating
   uint32_t padcnt[kPadWords];      // pass 0: counts of padding keys, by lane % kPadWords
-  uint2 list[kListCap + 1];        // (key, id) of the items in the pass-0 threshold bin, then
+  uint2 list[kListCap + 1];        // (score bits, id) of the items in the pass-0 threshold bin, then
                                    // one write-only dump slot for all other items
   uint32_t segment[2][kWaves];     // per-wave flagged counts (dup scan, select scan)
   uint32_t slices[3][kMaxSplit];   // split rows: per slice, keys above the threshold bin, selected
@@ -362,7 +363,7 @@ __device__ __forceinline__ void radix_pass(SelectLds<BLOCK>& lds, int pass, cons
 // (BY_ID false) or complemented ids of the list items whose key is `thr`.
 // ALL: every list item matches (the first key pass, whose list holds exactly
 // the items of the pass-0 threshold bin), so no item is tested and each reads
-// its (key, id) pair in one LDS load; an item past its digit's bucket writes
+// its (score bits, id) pair in one LDS load; an item past its digit's bucket writes
 // to a dump slot (the first word after the buckets, in hist[2], which no list
 // path uses) instead of branching.
 // Counts into small[q % 3] and, after its barrier, clears small[(q + 2) % 3]
@@ -386,15 +387,16 @@ __device__ __forceinline__ const uint2* list_pass(SelectLds<BLOCK>& lds, int q, 
   uint2* bucket = reinterpret_cast<uint2*>(&lds.hist[0][0]);
   for (int e = t; e < m; e += BLOCK) {
     const uint2 x = lds.list[e];
-    const uint32_t v = BY_ID ? ~x.y : x.x;
+    const uint32_t kx = score_key(x.x);
+    const uint32_t v = BY_ID ? ~x.y : kx;
     if constexpr (ALL) {
       const uint32_t d = (v >> SHIFT) & kDigitMask;
       const uint32_t r = lds_add(hist + d);
-      bucket[r < static_cast<uint32_t>(kBucket) ? d * kBucket + r : NB * kBucket] = make_uint2(x.x, ~x.y);
-    } else if ((!BY_ID || x.x == thr) && (v & st.mask) == st.prefix) {
+      bucket[r < static_cast<uint32_t>(kBucket) ? d * kBucket + r : NB * kBucket] = make_uint2(kx, ~x.y);
+    } else if ((!BY_ID || kx == thr) && (v & st.mask) == st.prefix) {
       const uint32_t d = (v >> SHIFT) & kDigitMask;
       const uint32_t r = lds_add(hist + d);
-      if (r < static_cast<uint32_t>(kBucket)) bucket[d * kBucket + r] = make_uint2(x.x, ~x.y);
+      if (r < static_cast<uint32_t>(kBucket)) bucket[d * kBucket + r] = make_uint2(kx, ~x.y);
     }
   }
   lds_barrier();
@@ -415,10 +417,10 @@ __device__ __forceinline__ const uint2* list_pass_ids(SelectLds<BLOCK>& lds, int
   for (int e = t; e < m; e += BLOCK) {
     const uint2 x = lds.list[e];
     const uint32_t v = ~x.y;
-    if (x.x == thr && (v & st.mask) == st.prefix) {
+    if (score_key(x.x) == thr && (v & st.mask) == st.prefix) {
       const uint32_t d = (v >> shift) & dmask;
       const uint32_t r = lds_add(hist + d);
-      if (r < static_cast<uint32_t>(kBucket)) bucket[d * kBucket + r] = make_uint2(x.x, v);
+      if (r < static_cast<uint32_t>(kBucket)) bucket[d * kBucket + r] = make_uint2(thr, v);
     }
   }
   lds_barrier();
@@ -537,8 +539,9 @@ __device__ __forceinline__ void list_common_bits(SelectLds<BLOCK>& lds, int m, i
   uint32_t a = 0u, b = ~0u, c = 0u, d = ~0u;
   for (int e = t; e < m; e += BLOCK) {
     const uint2 x = lds.list[e];
-    a |= x.x;
-    b &= x.x;
+    const uint32_t kx = score_key(x.x);
+    a |= kx;
+    b &= kx;
     c |= ~x.y;
     d &= ~x.y;
   }
@@ -1033,9 +1036,12 @@ __global__ __launch_bounds__(BLOCK) void stable_topk_kernel(Source src, Sink sin
   const uint32_t m = sk.count;  // items in the threshold bin
   bool tie = false, dup = false;
   Radix ik{0u, 0u, 0u, 0u};
-  // 3. the threshold bin as a list: each of its items writes itself at its
-  // pass-0 rank (every other item writes to one shared dump slot, so the loop
-  // has no per-item branch).  The list is built in a block of its own, ahead
+  // 3. the threshold bin as a list: each of its items writes its (score bits,
+  // id) pair, which sit in adjacent registers as loaded, at its pass-0 rank
+  // (every other item writes to one shared dump slot, so the loop has no
+  // per-item branch); the list passes recompute the keys of the few list items
+  // (writing keys instead takes a register copy per item: large 7.60 vs 7.58
+  // us, decode 16 rows 5.81 vs 5.78).  The list is built in a block of its own, ahead
   // of the choice between the list passes and the register passes, so that
   // the pass-0 ranks die before that branch (the scheduling barrier keeps the
   // compiler from merging the two blocks): each path then fits in 128 VGPRs,
@@ -1046,7 +1052,7 @@ __global__ __launch_bounds__(BLOCK) void stable_topk_kernel(Source src, Sink sin
 #pragma unroll
       for (int i = 0; i < N; ++i) {
         const bool in_bin = ok(i) && (key[i] >> 21) == d0;
-        lds.list[in_bin ? rank_in_bin[i] : static_cast<uint32_t>(kListCap)] = make_uint2(key[i], idv[i]);
+        lds.list[in_bin ? rank_in_bin[i] : static_cast<uint32_t>(kListCap)] = make_uint2(bits[i], idv[i]);
       }
     } else {
       // padding keys were ranked per lane word: they follow the bin's other
@@ -1058,7 +1064,7 @@ __global__ __launch_bounds__(BLOCK) void stable_topk_kernel(Source src, Sink sin
       for (int i = 0; i < N; ++i) {
         const bool in_bin = ok(i) && (key[i] >> 21) == d0;
         const uint32_t slot = rank_in_bin[i] + (key[i] == kPadKey ? pad_base : 0u);
-        lds.list[in_bin ? slot : static_cast<uint32_t>(kListCap)] = make_uint2(key[i], idv[i]);
+        lds.list[in_bin ? slot : static_cast<uint32_t>(kListCap)] = make_uint2(bits[i], idv[i]);
       }
     }
     lds_barrier();
@@ -1264,15 +1270,20 @@ __global__ __launch_bounds__(BLOCK) void stable_topk_kernel(Source src, Sink sin
   const uint32_t out_first = waves_before<BLOCK>(lds.segment[1], w);
   stamp<BLOCK>(11, w, lane);  // count exchange
   if (staged) {
-    // all reads first, then all stores; slots past out_count hold stale
-    // values, and their stores are dropped (the reads stay inside the wave's
-    // kStageCap + 64 slots)
+    // all reads first, then the stores of the copies that hold any of the
+    // wave's items: a store whose lanes all fall past out_count would write
+    // nothing but still cost its issue, so the copies past the count are
+    // skipped by a wave-uniform branch (measured: large 7.65 -> 7.60 us,
+    // short-context 7.13 -> 6.97); inside the last copy, lanes past out_count
+    // hold stale values and their stores are dropped (the reads stay inside
+    // the wave's kStageCap + 64 slots)
     constexpr int kCopies = (kStageCap + kWave - 1) / kWave;
     uint2 x[kCopies];
 #pragma unroll
     for (int u = 0; u < kCopies; ++u) x[u] = stage[w][u * kWave + lane];
 #pragma unroll
     for (int u = 0; u < kCopies; ++u) {
+      if (static_cast<uint32_t>(u * kWave) >= out_count) break;  // wave-uniform
       const uint32_t e = static_cast<uint32_t>(u * kWave + lane);
       dst.store(e < out_count, out_first + e, x[u].x, x[u].y);
     }
@@ -1607,6 +1618,7 @@ __global__ __launch_bounds__(BLOCK) void split_select_kernel(const dcp_topk_cand
     for (int u = 0; u < kCopies; ++u) x[u] = stage[w][u * kWave + lane];
 #pragma unroll
     for (int u = 0; u < kCopies; ++u) {
+      if (static_cast<uint32_t>(u * kWave) >= out_count) break;  // wave-uniform
       const uint32_t e = static_cast<uint32_t>(u * kWave + lane);
       dst.store(e < out_count, out_first + e, x[u].x, x[u].y);
     }
