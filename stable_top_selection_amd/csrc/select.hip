@@ -125,7 +125,12 @@ __device__ __forceinline__ void lds_barrier() {
 // own): lane 0 of the first and of the last wave of each of the first
 // kStampRows workgroups records the shader clock (s_memtime) at each phase
 // boundary of the select kernel, with a vector store into phase_stamps, which
-// dcptopk_phase_stamps copies out.  In every other build stamp() is empty.
+// dcptopk_phase_stamps copies out.  The first two boundaries (the wave's start
+// and the moment its first row loads issue) are only read into registers with
+// phase_clock() and stored after the first barrier with stamp_value(): a store
+// there would wait for the address of phase_stamps and hold back the kernel
+// argument and row loads behind it.  In every other build phase_clock()
+// returns 0 and stamp() and stamp_value() are empty.
 #ifndef DCPTOPK_PHASE_STAMPS
 #define DCPTOPK_PHASE_STAMPS 0
 #endif
@@ -135,13 +140,35 @@ constexpr int kStampSlots = 16;   // phase boundaries per wave
 __device__ unsigned long long phase_stamps[kStampRows * 2 * kStampSlots];
 #endif
 
+__device__ __forceinline__ unsigned long long phase_clock() {
+#if DCPTOPK_PHASE_STAMPS
+  __builtin_amdgcn_sched_barrier(0);  // the read stays where it is written
+  const unsigned long long now = __builtin_amdgcn_s_memtime();
+  __builtin_amdgcn_sched_barrier(0);
+  return now;
+#else
+  return 0;
+#endif
+}
+
+template <int BLOCK>
+__device__ __forceinline__ void stamp_value(int phase, int w, int lane, unsigned long long value) {
+#if DCPTOPK_PHASE_STAMPS
+  if (lane == 0 && (w == 0 || w == BLOCK / kWave - 1) && blockIdx.x < kStampRows)
+    phase_stamps[(blockIdx.x * 2 + (w != 0)) * kStampSlots + phase] = value;
+#else
+  (void)phase;
+  (void)w;
+  (void)lane;
+  (void)value;
+#endif
+}
+
 template <int BLOCK>
 __device__ __forceinline__ void stamp(int phase, int w, int lane) {
 #if DCPTOPK_PHASE_STAMPS
-  __builtin_amdgcn_sched_barrier(0);  // the stamp stays where it is written
-  const unsigned long long now = __builtin_amdgcn_s_memtime();
-  if (lane == 0 && (w == 0 || w == BLOCK / kWave - 1) && blockIdx.x < kStampRows)
-    phase_stamps[(blockIdx.x * 2 + (w != 0)) * kStampSlots + phase] = now;
+  const unsigned long long now = phase_clock();
+  stamp_value<BLOCK>(phase, w, lane, now);
   __builtin_amdgcn_sched_barrier(0);
 #else
   (void)phase;
@@ -919,6 +946,7 @@ __global__ __launch_bounds__(BLOCK) void stable_topk_kernel(Source src, Sink sin
   // wave's whole-row copy-out reads stay inside it when kStageCap < 64)
   constexpr int kStageCap = kWave * N / 2 < 448 ? kWave * N / 2 : 448;
   __shared__ uint2 stage[BLOCK / kWave][kStageCap + kWave];
+  const unsigned long long t_start = phase_clock();  // stamp 0: the wave starts
 
   const int t = threadIdx.x;
   const int lane = t & (kWave - 1);
@@ -926,7 +954,6 @@ __global__ __launch_bounds__(BLOCK) void stable_topk_kernel(Source src, Sink sin
   const int64_t row = blockIdx.x;
   const int C = src.count(row);
   const typename Sink::Row dst = sink.bind(row, k);
-  stamp<BLOCK>(0, w, lane);  // start
 
   // Wave w reads positions [w*64*N, (w+1)*64*N), 64*VEC consecutive ones per
   // load.
@@ -961,6 +988,7 @@ __global__ __launch_bounds__(BLOCK) void stable_topk_kernel(Source src, Sink sin
   // 5.89, short-context 7.49 -> 7.30, the 256-row batch unchanged; a quarter
   // or three quarters up front measured slower)
   constexpr int kEarly = Source::kChunkLoads && NV >= 8 ? NV / 2 : NV;  // chunks loaded up front
+  const unsigned long long t_loads = phase_clock();  // stamp 1: arguments read, row loads about to issue
   if constexpr (kEarly < NV) {
 #pragma unroll
     for (int v = 0; v < kEarly; ++v) src.template load_chunk<VEC>(row, first, C, v, bits, idv);
@@ -975,7 +1003,9 @@ __global__ __launch_bounds__(BLOCK) void stable_topk_kernel(Source src, Sink sin
   if (t < 4) lds.common[t] = (t & 1) ? ~0u : 0u;  // OR slots 0, AND slots ~0 (list_common_bits)
   lds_barrier();
   __builtin_amdgcn_sched_barrier(0);
-  stamp<BLOCK>(1, w, lane);  // loads issued, LDS cleared, first barrier
+  stamp<BLOCK>(2, w, lane);  // loads issued, LDS cleared, first barrier
+  stamp_value<BLOCK>(0, w, lane, t_start);
+  stamp_value<BLOCK>(1, w, lane, t_loads);
 
   // FULL: the row fills every slot (C == BLOCK*N); else the last are masked
   // out: item i is valid if its position, first + (i / VEC) * kChunk + i % VEC,
@@ -1021,17 +1051,17 @@ __global__ __launch_bounds__(BLOCK) void stable_topk_kernel(Source src, Sink sin
     if constexpr (!FULL) target = ok(i) ? target : spare;
     rank_in_bin[i] = lds_add(target);
   }
-  stamp<BLOCK>(2, w, lane);  // pass-0 atomics issued
+  stamp<BLOCK>(3, w, lane);  // pass-0 atomics issued
   lds_barrier();
   // padding keys counted in pass 0, in total and in the words before this lane's
-  stamp<BLOCK>(3, w, lane);  // pass-0 barrier
+  stamp<BLOCK>(4, w, lane);  // pass-0 barrier
   const uint4 pw0 = *reinterpret_cast<const uint4*>(lds.padcnt);
   const uint4 pw1 = *reinterpret_cast<const uint4*>(lds.padcnt + 4);
   const uint32_t pad_total = pw0.x + pw0.y + pw0.z + pw0.w + pw1.x + pw1.y + pw1.z + pw1.w;
   static_assert(kPadWords == 8, "two uint4 reads");
   Radix sk{0u, 0u, static_cast<uint32_t>(k), 0u};
   advance(sk, find_digit_pass0(lds.hist[0], sk.need, lane, kPadBin, pad_total), 21, 0x7FFu);
-  stamp<BLOCK>(4, w, lane);  // digit search
+  stamp<BLOCK>(5, w, lane);  // digit search
 
   const uint32_t m = sk.count;  // items in the threshold bin
   bool tie = false, dup = false;
@@ -1070,11 +1100,11 @@ __global__ __launch_bounds__(BLOCK) void stable_topk_kernel(Source src, Sink sin
     lds_barrier();
   }
   __builtin_amdgcn_sched_barrier(0);
-  stamp<BLOCK>(5, w, lane);  // list built
+  stamp<BLOCK>(6, w, lane);  // list built
   if (m != sk.need && m <= kListCap) {
     // then list pass 0 counts the next 8 key bits
     const uint2* items = list_pass<BLOCK, 13, 8, false, true>(lds, 0, m, 0u, sk, t, lane);
-    stamp<BLOCK>(6, w, lane);  // first list pass
+    stamp<BLOCK>(7, w, lane);  // first list pass
     int q = 1;
     bool same_ids_known = false, resolved = false;
     uint32_t uor = 0u, uand = 0u;
@@ -1212,7 +1242,7 @@ __global__ __launch_bounds__(BLOCK) void stable_topk_kernel(Source src, Sink sin
     }
   }
 
-  stamp<BLOCK>(7, w, lane);  // threshold resolved
+  stamp<BLOCK>(8, w, lane);  // threshold resolved
   uint32_t duprank[N];
   if (dup) {
     uint32_t same[N];
@@ -1252,10 +1282,10 @@ __global__ __launch_bounds__(BLOCK) void stable_topk_kernel(Source src, Sink sin
   // the loop has no per-item branch) while the waves' counts are exchanged,
   // then writes its range with consecutive stores.  A wave with more selected
   // items than its area stores every item at its rank from the registers.
-  stamp<BLOCK>(8, w, lane);  // selection flags
+  stamp<BLOCK>(9, w, lane);  // selection flags
   uint32_t rank[N];
   const uint32_t out_count = wave_rank<VEC, N>(sel, rank, lane);
-  stamp<BLOCK>(9, w, lane);  // ranks
+  stamp<BLOCK>(10, w, lane);  // ranks
   if (lane == 0) lds.segment[1][w] = out_count;
   const bool staged = out_count <= static_cast<uint32_t>(kStageCap);  // wave-uniform
   if (staged) {
@@ -1265,10 +1295,10 @@ __global__ __launch_bounds__(BLOCK) void stable_topk_kernel(Source src, Sink sin
       stage[w][slot] = make_uint2(bits[i], idv[i]);
     }
   }
-  stamp<BLOCK>(10, w, lane);  // staging writes
+  stamp<BLOCK>(11, w, lane);  // staging writes
   lds_barrier();
   const uint32_t out_first = waves_before<BLOCK>(lds.segment[1], w);
-  stamp<BLOCK>(11, w, lane);  // count exchange
+  stamp<BLOCK>(12, w, lane);  // count exchange
   if (staged) {
     // all reads first, then the stores of the copies that hold any of the
     // wave's items: a store whose lanes all fall past out_count would write
@@ -1291,7 +1321,7 @@ __global__ __launch_bounds__(BLOCK) void stable_topk_kernel(Source src, Sink sin
 #pragma unroll
     for (int i = 0; i < N; ++i) dst.store(sel[i] != 0u, out_first + rank[i], bits[i], idv[i]);
   }
-  stamp<BLOCK>(12, w, lane);  // stores issued
+  stamp<BLOCK>(13, w, lane);  // stores issued
 }
 
 // ---------------------------------------------------------------------------

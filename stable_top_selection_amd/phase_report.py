@@ -34,9 +34,9 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
-PHASES = ["loads issued, LDS cleared, first barrier", "pass-0 atomics issued", "pass-0 barrier", "digit search",
-          "list built", "first list pass", "threshold resolved", "selection flags", "ranks", "staging writes",
-          "count exchange", "stores issued"]
+PHASES = ["kernel arguments read, row addresses computed", "loads issued, LDS cleared, first barrier",
+          "pass-0 atomics issued", "pass-0 barrier", "digit search", "list built", "first list pass",
+          "threshold resolved", "selection flags", "ranks", "staging writes", "count exchange", "stores issued"]
 SLOTS = 16  # stamps per wave in the library's array
 STAMP_ROWS = 1024
 POOL_BYTES = 2 * (256 + 32) * (1 << 20)
@@ -56,6 +56,12 @@ def _timelines(st: np.ndarray, rows: int):
             ends.append(None if (a == 0 and b == 0) else (int(max(a, b) - t0), int(b - a)))
         out.append(ends)
     return out
+
+
+def _start_lags(st: np.ndarray, rows: int):
+    """Per row: how many cycles after wave 0 the last wave started."""
+    st = st.reshape(STAMP_ROWS, 2, SLOTS)[:rows].astype(np.int64)
+    return [int(st[r, 1, 0] - st[r, 0, 0]) for r in range(rows)]
 
 
 def _summarise(lines):
@@ -143,12 +149,14 @@ def main() -> None:
     # the caches by the time the last is written: cold samples take those
     torch.cuda.synchronize()
     read()  # clear
-    cold, warm = [], []
+    cold, warm, lag_cold, lag_warm = [], [], [], []
     for s in range(args.samples):
         launch(pool[s])
         cold += read()
+        lag_cold += _start_lags(stamps, rows)
         launch(pool[s])
         warm += read()
+        lag_warm += _start_lags(stamps, rows)
     print(f"workload {name}: {rows} rows x {num_cand} candidates, k {k}; "
           f"{args.samples} launches per mode, medians over rows x launches, shader-clock cycles from wave 0's start")
     print()
@@ -159,6 +167,9 @@ def main() -> None:
         fmt = lambda x: "-" if x is None else f"{x:,.0f}"  # noqa: E731
         print(f"| {name} | {c[0]} / {len(cold)} | {fmt(c[1])} | {fmt(c[2])} | {fmt(c[3])} | {fmt(w[1])} | "
               f"{fmt(w[2])} |")
+    print()
+    print(f"Start of the workgroup's last wave behind its wave 0 (median, cycles): cold "
+          f"{statistics.median(lag_cold):,.0f}, warm {statistics.median(lag_warm):,.0f}")
 
 
 if __name__ == "__main__":

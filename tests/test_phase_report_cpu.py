@@ -34,3 +34,7 @@ def test_skipped_phase_is_bridged():
     assert res[6][0] == 3
     # row 1's next length spans both phases: lengths 100, 200, 100 -> median 100
     assert res[6][2] == 100
+
+
+def test_start_lags():
+    assert P._start_lags(_stamps(3), 3) == [7, 14, 21]
