@@ -32,6 +32,11 @@ PHASE_FLAGS = ["-DDCPTOPK_PHASE_STAMPS=1"]
 SANITIZED_LIB_PATH = os.path.join(PKG, "libdcptopk_host_sanitized.so")
 SANITIZE_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
                   "-Xarch_host", "-fno-sanitize-recover=all", "-Xarch_host", "-fno-omit-frame-pointer"]
+# reference kernels for the select's roofline (an empty launch, and a bare read
+# and write of the headline's bytes), not part of the library; timed by
+# stable_top_selection_amd.floor_probe
+FLOOR_LIB_PATH = os.path.join(PKG, "libdcptopk_floor.so")
+FLOOR_SOURCES = [os.path.join(PKG, "probes", "floor.hip")]
 # per-kernel register, scratch, occupancy and LDS figures of the last build,
 # from the compiler's resource-usage remarks
 RESOURCES_PATH = os.path.join(PKG, "libdcptopk.kernels.tsv")
@@ -100,9 +105,12 @@ def sources() -> list[str]:
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith((".hip", ".cpp")))
 
 
-def build(verbose: bool = False, extra_flags: list[str] | None = None, out: str = LIB_PATH) -> str:
-    """Compile and link the library; returns the path of the shared object."""
-    cmd = [hipcc(), *HIPCC_FLAGS, *(extra_flags or []), f"-I{INCLUDE}", "-shared", *sources(), "-o", out + ".tmp"]
+def build(verbose: bool = False, extra_flags: list[str] | None = None, out: str = LIB_PATH,
+          srcs: list[str] | None = None) -> str:
+    """Compile and link the library (or `srcs` into `out`); returns the path
+    of the shared object."""
+    cmd = [hipcc(), *HIPCC_FLAGS, *(extra_flags or []), f"-I{INCLUDE}", "-shared", *(srcs or sources()), "-o",
+           out + ".tmp"]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -123,15 +131,17 @@ def build(verbose: bool = False, extra_flags: list[str] | None = None, out: str 
 
 def build_all(verbose: bool = False) -> list[str]:
     """The four libraries (product, race-stress test build, phase-stamp build,
-    host-sanitized build), compiled concurrently."""
+    host-sanitized build) and the roofline reference kernels, compiled
+    concurrently."""
     from concurrent.futures import ThreadPoolExecutor
 
-    with ThreadPoolExecutor(max_workers=4) as pool:
+    with ThreadPoolExecutor(max_workers=5) as pool:
         main = pool.submit(build, verbose)
         stress = pool.submit(build, False, STRESS_FLAGS, STRESS_LIB_PATH)
         phases = pool.submit(build, False, PHASE_FLAGS, PHASES_LIB_PATH)
         sanitized = pool.submit(build, False, SANITIZE_FLAGS, SANITIZED_LIB_PATH)
-        return [main.result(), stress.result(), phases.result(), sanitized.result()]
+        floor = pool.submit(build, False, None, FLOOR_LIB_PATH, FLOOR_SOURCES)
+        return [main.result(), stress.result(), phases.result(), sanitized.result(), floor.result()]
 
 
 if __name__ == "__main__":
