@@ -2,7 +2,7 @@
 against the oracle.
 
 The other GPU tests pick their shapes by hand (tile boundaries, the pages'
-workloads, degenerate rows).  Here one fixed seed draws a few hundred more:
+workloads, degenerate rows).  Here fixed seeds draw about a thousand more:
 candidate counts log-uniform over [1, 16384], k below, near and above the
 count, five score distributions with optional padding and repeated ids,
 misaligned buffers, the split-row path at 1 to 8 parts, the local top-K with
@@ -63,7 +63,7 @@ def _compare(gb, gi, scores, ids, k, label):
         raise AssertionError(f"{label}: {len(bad)} rows differ, first {int(bad[0])}")
 
 
-@pytest.mark.parametrize("block", range(6))
+@pytest.mark.parametrize("block", range(24))
 def test_select_random_shapes(block):
     rng = np.random.default_rng(7000 + block)
     for case in range(25):
@@ -77,7 +77,7 @@ def test_select_random_shapes(block):
         _compare(gb, gi, g.scores, g.ids, k, label)
 
 
-@pytest.mark.parametrize("block", range(2))
+@pytest.mark.parametrize("block", range(6))
 def test_split_random_shapes(block):
     rng = np.random.default_rng(7100 + block)
     for case in range(20):
@@ -91,8 +91,9 @@ def test_split_random_shapes(block):
         _compare(gb, gi, g.scores, g.ids, k, label)
 
 
-def test_local_random_shapes():
-    rng = np.random.default_rng(7200)
+@pytest.mark.parametrize("block", range(3))
+def test_local_random_shapes(block):
+    rng = np.random.default_rng(7200 + block)
     for case in range(30):
         cols = _count(rng)
         k = _k(rng, cols)
@@ -100,7 +101,7 @@ def test_local_random_shapes():
         dist = ["normal", "levels", "special"][int(rng.integers(0, 3))]
         lengths = bool(rng.random() < 0.5)
         d = W.local(rows=rows, num_cols=cols, k=k, seed=int(rng.integers(1 << 30)), dist=dist, with_lengths=lengths)
-        label = f"local case {case}: {d.name} lengths={lengths}"
+        label = f"local block {block} case {case}: {d.name} lengths={lengths}"
         print(label, flush=True)
         os_, oi = B.local_topk(to_dev(d.scores), d.k, lengths=to_dev(d.lengths) if lengths else None)
         torch.cuda.synchronize()
@@ -109,8 +110,9 @@ def test_local_random_shapes():
         assert np.array_equal(oi.cpu().numpy(), wi), label
 
 
-def test_fused_random_shapes():
-    rng = np.random.default_rng(7300)
+@pytest.mark.parametrize("block", range(3))
+def test_fused_random_shapes(block):
+    rng = np.random.default_rng(7300 + block)
     for case in range(20):
         dcp = int(rng.integers(1, 17))
         local_k = 64 * int(rng.integers(1, 16384 // (64 * dcp) + 1))
@@ -122,7 +124,7 @@ def test_fused_random_shapes():
         idx = np.where(rng.random(idx.shape) < float(rng.choice([0.0, 0.1, 0.6])), np.int32(-1), idx).astype(np.int32)
         starts = rng.integers(0, 1 << 20, size=(dcp, rows), dtype=np.int32)
         offs = (np.arange(dcp) * (1 << 22)).astype(np.int32)
-        label = f"fused case {case}: dcp={dcp} local_k={local_k} rows={rows} k={k}"
+        label = f"fused block {block} case {case}: dcp={dcp} local_k={local_k} rows={rows} k={k}"
         print(label, flush=True)
         out = B.merge_fused([to_dev(scores[r]) for r in range(dcp)], [to_dev(idx[r]) for r in range(dcp)],
                             [to_dev(starts[r]) for r in range(dcp)], [int(x) for x in offs], k)
