@@ -125,12 +125,14 @@ __device__ __forceinline__ void lds_barrier() {
 // own): lane 0 of the first and of the last wave of each of the first
 // kStampRows workgroups records the shader clock (s_memtime) at each phase
 // boundary of the select kernel, with a vector store into phase_stamps, which
-// dcptopk_phase_stamps copies out.  The first two boundaries (the wave's start
-// and the moment its first row loads issue) are only read into registers with
-// phase_clock() and stored after the first barrier with stamp_value(): a store
-// there would wait for the address of phase_stamps and hold back the kernel
-// argument and row loads behind it.  In every other build phase_clock()
-// returns 0 and stamp() and stamp_value() are empty.
+// dcptopk_phase_stamps copies out.  A stamped wave finds its slots once, while
+// its first loads are in flight (stamp_slots); a stamp is then the clock read,
+// its wait and one store (about 64 cycles; looking the slots up at every stamp
+// took about 220).  The first two boundaries (the wave's start and the moment
+// its first row loads issue) are only read into registers with phase_clock()
+// and stored after the first barrier with stamp_value(), so that nothing holds
+// back the kernel argument and row loads.  In every other build stamp_slots()
+// and phase_clock() return 0 and the stamps compile to nothing.
 #ifndef DCPTOPK_PHASE_STAMPS
 #define DCPTOPK_PHASE_STAMPS 0
 #endif
@@ -139,6 +141,19 @@ constexpr int kStampRows = 1024;  // workgroups stamped
 constexpr int kStampSlots = 16;   // phase boundaries per wave
 __device__ unsigned long long phase_stamps[kStampRows * 2 * kStampSlots];
 #endif
+
+// This wave's stamp slots if it is stamped (wave-uniform), else null.
+template <int BLOCK>
+__device__ __forceinline__ unsigned long long* stamp_slots(int w) {
+#if DCPTOPK_PHASE_STAMPS
+  return (w == 0 || w == BLOCK / kWave - 1) && blockIdx.x < kStampRows
+             ? phase_stamps + (blockIdx.x * 2 + (w != 0)) * kStampSlots
+             : nullptr;
+#else
+  (void)w;
+  return nullptr;
+#endif
+}
 
 __device__ __forceinline__ unsigned long long phase_clock() {
 #if DCPTOPK_PHASE_STAMPS
@@ -151,28 +166,25 @@ __device__ __forceinline__ unsigned long long phase_clock() {
 #endif
 }
 
-template <int BLOCK>
-__device__ __forceinline__ void stamp_value(int phase, int w, int lane, unsigned long long value) {
+__device__ __forceinline__ void stamp_value(unsigned long long* slots, int phase, int lane, unsigned long long value) {
 #if DCPTOPK_PHASE_STAMPS
-  if (lane == 0 && (w == 0 || w == BLOCK / kWave - 1) && blockIdx.x < kStampRows)
-    phase_stamps[(blockIdx.x * 2 + (w != 0)) * kStampSlots + phase] = value;
+  if (slots != nullptr && lane == 0) slots[phase] = value;
 #else
+  (void)slots;
   (void)phase;
-  (void)w;
   (void)lane;
   (void)value;
 #endif
 }
 
-template <int BLOCK>
-__device__ __forceinline__ void stamp(int phase, int w, int lane) {
+__device__ __forceinline__ void stamp(unsigned long long* slots, int phase, int lane) {
 #if DCPTOPK_PHASE_STAMPS
   const unsigned long long now = phase_clock();
-  stamp_value<BLOCK>(phase, w, lane, now);
+  stamp_value(slots, phase, lane, now);
   __builtin_amdgcn_sched_barrier(0);
 #else
+  (void)slots;
   (void)phase;
-  (void)w;
   (void)lane;
 #endif
 }
@@ -996,6 +1008,8 @@ __global__ __launch_bounds__(BLOCK) void stable_topk_kernel(Source src, Sink sin
     src.template load<VEC, NV>(row, first, C, bits, idv, aux);
   }
 
+  // (the stamp slots' address is looked up while the loads are in flight)
+  unsigned long long* const stamps = stamp_slots<BLOCK>(w);
   // clear the histograms while the loads are in flight; the key transform
   // stays after the barrier so that pass 0 starts on the first chunk while
   // later chunks are still arriving
@@ -1003,9 +1017,9 @@ __global__ __launch_bounds__(BLOCK) void stable_topk_kernel(Source src, Sink sin
   if (t < 4) lds.common[t] = (t & 1) ? ~0u : 0u;  // OR slots 0, AND slots ~0 (list_common_bits)
   lds_barrier();
   __builtin_amdgcn_sched_barrier(0);
-  stamp<BLOCK>(2, w, lane);  // loads issued, LDS cleared, first barrier
-  stamp_value<BLOCK>(0, w, lane, t_start);
-  stamp_value<BLOCK>(1, w, lane, t_loads);
+  stamp(stamps, 2, lane);  // loads issued, LDS cleared, first barrier
+  stamp_value(stamps, 0, lane, t_start);
+  stamp_value(stamps, 1, lane, t_loads);
 
   // FULL: the row fills every slot (C == BLOCK*N); else the last are masked
   // out: item i is valid if its position, first + (i / VEC) * kChunk + i % VEC,
@@ -1051,17 +1065,17 @@ __global__ __launch_bounds__(BLOCK) void stable_topk_kernel(Source src, Sink sin
     if constexpr (!FULL) target = ok(i) ? target : spare;
     rank_in_bin[i] = lds_add(target);
   }
-  stamp<BLOCK>(3, w, lane);  // pass-0 atomics issued
+  stamp(stamps, 3, lane);  // pass-0 atomics issued
   lds_barrier();
   // padding keys counted in pass 0, in total and in the words before this lane's
-  stamp<BLOCK>(4, w, lane);  // pass-0 barrier
+  stamp(stamps, 4, lane);  // pass-0 barrier
   const uint4 pw0 = *reinterpret_cast<const uint4*>(lds.padcnt);
   const uint4 pw1 = *reinterpret_cast<const uint4*>(lds.padcnt + 4);
   const uint32_t pad_total = pw0.x + pw0.y + pw0.z + pw0.w + pw1.x + pw1.y + pw1.z + pw1.w;
   static_assert(kPadWords == 8, "two uint4 reads");
   Radix sk{0u, 0u, static_cast<uint32_t>(k), 0u};
   advance(sk, find_digit_pass0(lds.hist[0], sk.need, lane, kPadBin, pad_total), 21, 0x7FFu);
-  stamp<BLOCK>(5, w, lane);  // digit search
+  stamp(stamps, 5, lane);  // digit search
 
   const uint32_t m = sk.count;  // items in the threshold bin
   bool tie = false, dup = false;
@@ -1100,11 +1114,11 @@ __global__ __launch_bounds__(BLOCK) void stable_topk_kernel(Source src, Sink sin
     lds_barrier();
   }
   __builtin_amdgcn_sched_barrier(0);
-  stamp<BLOCK>(6, w, lane);  // list built
+  stamp(stamps, 6, lane);  // list built
   if (m != sk.need && m <= kListCap) {
     // then list pass 0 counts the next 8 key bits
     const uint2* items = list_pass<BLOCK, 13, 8, false, true>(lds, 0, m, 0u, sk, t, lane);
-    stamp<BLOCK>(7, w, lane);  // first list pass
+    stamp(stamps, 7, lane);  // first list pass
     int q = 1;
     bool same_ids_known = false, resolved = false;
     uint32_t uor = 0u, uand = 0u;
@@ -1242,7 +1256,7 @@ __global__ __launch_bounds__(BLOCK) void stable_topk_kernel(Source src, Sink sin
     }
   }
 
-  stamp<BLOCK>(8, w, lane);  // threshold resolved
+  stamp(stamps, 8, lane);  // threshold resolved
   uint32_t duprank[N];
   if (dup) {
     uint32_t same[N];
@@ -1282,10 +1296,10 @@ __global__ __launch_bounds__(BLOCK) void stable_topk_kernel(Source src, Sink sin
   // the loop has no per-item branch) while the waves' counts are exchanged,
   // then writes its range with consecutive stores.  A wave with more selected
   // items than its area stores every item at its rank from the registers.
-  stamp<BLOCK>(9, w, lane);  // selection flags
+  stamp(stamps, 9, lane);  // selection flags
   uint32_t rank[N];
   const uint32_t out_count = wave_rank<VEC, N>(sel, rank, lane);
-  stamp<BLOCK>(10, w, lane);  // ranks
+  stamp(stamps, 10, lane);  // ranks
   if (lane == 0) lds.segment[1][w] = out_count;
   const bool staged = out_count <= static_cast<uint32_t>(kStageCap);  // wave-uniform
   if (staged) {
@@ -1295,10 +1309,10 @@ __global__ __launch_bounds__(BLOCK) void stable_topk_kernel(Source src, Sink sin
       stage[w][slot] = make_uint2(bits[i], idv[i]);
     }
   }
-  stamp<BLOCK>(11, w, lane);  // staging writes
+  stamp(stamps, 11, lane);  // staging writes
   lds_barrier();
   const uint32_t out_first = waves_before<BLOCK>(lds.segment[1], w);
-  stamp<BLOCK>(12, w, lane);  // count exchange
+  stamp(stamps, 12, lane);  // count exchange
   if (staged) {
     // all reads first, then the stores of the copies that hold any of the
     // wave's items: a store whose lanes all fall past out_count would write
@@ -1321,7 +1335,7 @@ __global__ __launch_bounds__(BLOCK) void stable_topk_kernel(Source src, Sink sin
 #pragma unroll
     for (int i = 0; i < N; ++i) dst.store(sel[i] != 0u, out_first + rank[i], bits[i], idv[i]);
   }
-  stamp<BLOCK>(13, w, lane);  // stores issued
+  stamp(stamps, 13, lane);  // stores issued
 }
 
 // ---------------------------------------------------------------------------
