@@ -12,7 +12,7 @@
 // buffer is cleared only one full barrier after its last read and refilled one
 // barrier after that.
 //
-// One workgroup (256 or 512 threads: 4 or 8 wave64s) owns one row.  Every
+// One workgroup (256, 512 or 1024 threads: 4, 8 or 16 wave64s) owns one row.  Every
 // thread keeps N candidates in VGPRs for the whole kernel: wave w holds the
 // positions [w*64*N, (w+1)*64*N), its lane l the positions w*64*N +
 // v*64*VEC + VEC*l + j (chunk v < N/VEC, j < VEC), so the row is read from
@@ -52,7 +52,8 @@
 //      candidate-position order.  A wave's selected items fill one contiguous
 //      output range, so each wave stages them in its own LDS area at their rank
 //      inside the wave while the waves' counts are exchanged (one barrier),
-//      then writes its range with consecutive stores.  (A wave with more
+//      then writes its range with consecutive stores, 64 items per store and
+//      none past its count.  (A wave with more
 //      selected items than its staging area stores every item at its rank
 //      straight from registers; unselected items store to an offset past the
 //      buffer's range, which the hardware drops, so no loop has a per-item
