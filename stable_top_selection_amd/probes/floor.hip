@@ -55,6 +55,8 @@ __global__ __launch_bounds__(kBlock) void floor_stream_kernel(const u32x4* __res
 
 }  // namespace
 
+// Entry points return 0, -1 for an invalid argument (nothing launched) or -4
+// when the HIP runtime rejects the launch (the codes of libdcptopk).
 extern "C" {
 
 // One launch of `workgroups` empty workgroups of `threads` threads (1 to 1024).
