@@ -1,0 +1,109 @@
+"""The entry points from several host threads at once, each on its own stream.
+
+The header promises that every call only enqueues work on its stream and keeps
+no state (the static-scratch merge aside), so calls from several host threads
+on several streams are safe.  Here four threads each run the select, the
+split-row select (own workspace), the fused merge, the chunked merge (own
+workspace) and the local top-K on their own inputs, several rounds each, with
+the ctypes calls (which release the GIL) and the kernels of different streams
+overlapping; every result is then compared with the oracle bit for bit.
+"""
+import threading
+
+import numpy as np
+import pytest
+import torch
+
+from gpu_helpers import DEV, to_dev
+from oracle import stable_topk as O
+from stable_top_selection_amd import binding as B
+from stable_top_selection_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+THREADS = 4
+ROUNDS = 3
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    B.load_library()
+
+
+def _inputs(tid, rnd):
+    seed = 1000 * tid + rnd
+    sel = W.random_gathered(48, 8192, 2048, seed=seed, dist=["normal", "levels", "uniform"][(tid + rnd) % 3])
+    split = W.random_gathered(3, 8192, 1500, seed=seed + 500, dist="levels")
+    fused = W.prefill(rows=40, local_k=1024, seed=seed)
+    chunked = W.prefill(rows=1100, local_k=1024, seed=seed + 7)
+    local = W.local(rows=24, num_cols=4096, k=2048, seed=seed, with_lengths=bool(rnd % 2))
+    return sel, split, fused, chunked, local
+
+
+def _ranks(sh):
+    return ([to_dev(sh.scores[r]) for r in range(sh.dcp)], [to_dev(sh.local_idx[r]) for r in range(sh.dcp)],
+            [to_dev(sh.row_starts[r]) for r in range(sh.dcp)], [int(x) for x in sh.rank_offsets])
+
+
+def test_entry_points_from_several_threads_and_streams():
+    cases = [[_inputs(t, r) for r in range(ROUNDS)] for t in range(THREADS)]
+    # device copies made on the default stream, before any worker stream uses them
+    dev_in = [[(to_dev(sel.interleaved()), to_dev(split.interleaved()), _ranks(fused), _ranks(chunked),
+                to_dev(local.scores), to_dev(local.lengths) if local.lengths is not None else None)
+               for sel, split, fused, chunked, local in per] for per in cases]
+    torch.cuda.synchronize()
+    results = [[None] * ROUNDS for _ in range(THREADS)]
+    errors = []
+    start = threading.Barrier(THREADS)
+
+    def work(tid):
+        try:
+            stream = torch.cuda.Stream(device=DEV)
+            stream.wait_stream(torch.cuda.default_stream(DEV))
+            with torch.cuda.stream(stream):
+                start.wait()
+                for rnd in range(ROUNDS):
+                    sel, split, fused, chunked, local = cases[tid][rnd]
+                    cand, scand, franks, cranks, lscores, llens = dev_in[tid][rnd]
+                    ws = B.select_split_workspace(split.rows, split.num_cand, 4, DEV)
+                    cws = torch.empty(B.merge_workspace_bytes(chunked.rows, chunked.dcp, chunked.local_k),
+                                      dtype=torch.uint8, device=DEV)
+                    results[tid][rnd] = (
+                        B.select(cand, sel.k),
+                        B.select_split(scand, split.k, 4, workspace=ws),
+                        B.merge_fused(*franks, fused.k),
+                        B.merge_chunked(*cranks, chunked.k, workspace=cws),
+                        B.local_topk(lscores, local.k, lengths=llens),
+                    )
+            stream.synchronize()
+        except Exception as e:  # reported on the main thread
+            errors.append((tid, repr(e)))
+
+    threads = [threading.Thread(target=work, args=(t,)) for t in range(THREADS)]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join(timeout=120)
+    assert not any(th.is_alive() for th in threads), "a worker thread did not finish"
+    assert not errors, errors
+    torch.cuda.synchronize()
+
+    for tid in range(THREADS):
+        for rnd in range(ROUNDS):
+            sel, split, fused, chunked, local = cases[tid][rnd]
+            out_sel, out_split, out_fused, out_chunked, (ls, li) = results[tid][rnd]
+            label = f"thread {tid} round {rnd}"
+            for g, out in ((sel, out_sel), (split, out_split)):
+                ws_, wi = O.select(g.scores, g.ids, g.k)
+                o = out.cpu().numpy()
+                assert np.array_equal(o[..., 0].view(np.uint32), ws_.view(np.uint32)), f"{label}: {g.name}"
+                assert np.array_equal(o[..., 1], wi), f"{label}: {g.name}"
+            for sh, out in ((fused, out_fused), (chunked, out_chunked)):
+                ws_, wi = O.merge(sh.scores, sh.local_idx, sh.row_starts, sh.rank_offsets, sh.k)
+                o = out.cpu().numpy()
+                assert np.array_equal(o[..., 0].view(np.uint32), ws_.view(np.uint32)), f"{label}: merge T={sh.rows}"
+                assert np.array_equal(o[..., 1], wi), f"{label}: merge T={sh.rows}"
+            ws_, wi = O.local_topk(local.scores, local.k, local.lengths)
+            assert np.array_equal(ls.cpu().numpy().view(np.uint32), ws_.view(np.uint32)), f"{label}: local"
+            assert np.array_equal(li.cpu().numpy(), wi), f"{label}: local"
