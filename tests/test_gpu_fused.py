@@ -171,8 +171,9 @@ def test_fused_equals_chunked_on_ties():
 
 
 def test_fused_graph_replay():
-    """Captured into a HIP graph and replayed three times, with eager work and
-    a synchronisation between replays: every replay matches the oracle."""
+    """Captured into a HIP graph and replayed with new contents in the same
+    rank arrays before each replay (eager copies and a synchronisation in
+    between): every replay matches the oracle on its own inputs."""
     sh = W.prefill(rows=64, seed=77)
     sc, ix, rs, offs = _dev_shards(sh)
     out = torch.empty((64, 2048, 2), dtype=torch.int32, device=DEV)
@@ -181,11 +182,16 @@ def test_fused_graph_replay():
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         B.merge_fused(sc, ix, rs, offs, 2048, out=out)
-    want_s, want_i = O.merge(sh.scores, sh.local_idx, sh.row_starts, sh.rank_offsets, 2048)
-    for rep in range(3):
+    for rep, seed in enumerate((77, 78, 79)):
+        new = W.prefill(rows=64, seed=seed, invalid_frac=0.1 * rep)
+        for r in range(new.dcp):
+            sc[r].copy_(to_dev(new.scores[r]))
+            ix[r].copy_(to_dev(new.local_idx[r]))
+            rs[r].copy_(to_dev(new.row_starts[r]))
         out.fill_(0)
         g.replay()
         torch.cuda.synchronize()
+        want_s, want_i = O.merge(new.scores, new.local_idx, new.row_starts, new.rank_offsets, 2048)
         _assert_rows(out.cpu().numpy(), want_s, want_i, np.arange(64), f"graph replay {rep}")
 
 

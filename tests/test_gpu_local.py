@@ -138,3 +138,36 @@ def test_local_errors():
     with pytest.raises(B.DcpTopkError) as e:
         B.local_topk(s, 8, out_scores=out_s, out_idx=alias_i)
     assert e.value.status == B.EINVAL
+
+
+def test_local_graph_replay_with_changing_inputs():
+    """Captured into a HIP graph once; before each replay the scores and the
+    per-row lengths are overwritten in place (eager copies, a synchronisation
+    in between): every replay matches the oracle on its own inputs."""
+    rows, cols, k = 32, 4096, 2048
+    scores = torch.empty((rows, cols), dtype=torch.float32, device=DEV)
+    lengths = torch.empty((rows,), dtype=torch.int32, device=DEV)
+    os_ = torch.empty((rows, k), dtype=torch.float32, device=DEV)
+    oi = torch.empty((rows, k), dtype=torch.int32, device=DEV)
+    d0 = W.local(rows=rows, num_cols=cols, k=k, seed=90, with_lengths=True)
+    scores.copy_(to_dev(d0.scores))
+    lengths.copy_(to_dev(d0.lengths))
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        B.local_topk(scores, k, lengths=lengths, out_scores=os_, out_idx=oi)  # outside the graph
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        B.local_topk(scores, k, lengths=lengths, out_scores=os_, out_idx=oi)
+    for seed, dist in ((91, "normal"), (92, "levels"), (93, "special")):
+        d = W.local(rows=rows, num_cols=cols, k=k, seed=seed, dist=dist, with_lengths=True)
+        scores.copy_(to_dev(d.scores))
+        lengths.copy_(to_dev(d.lengths))
+        os_.fill_(0.0)
+        g.replay()
+        torch.cuda.synchronize()
+        ws, wi = O.local_topk(d.scores, k, d.lengths)
+        assert np.array_equal(os_.cpu().numpy().view(np.uint32), ws.view(np.uint32)), f"replay {seed}"
+        assert np.array_equal(oi.cpu().numpy(), wi), f"replay {seed}"
