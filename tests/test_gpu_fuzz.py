@@ -7,8 +7,11 @@ candidate counts log-uniform over [1, 16384], k below, near and above the
 count, five score distributions with optional padding and repeated ids,
 misaligned buffers, the split-row path at 1 to 8 parts, the local top-K with
 and without per-row lengths, and the fused merge over 1 to 16 ranks.  Each
-case prints its parameters before it runs.
+case prints its parameters before it runs.  DCPTOPK_FUZZ_SCALE=n runs n times
+as many blocks of cases (the first blocks are always the default run's).
 """
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -21,6 +24,7 @@ from stable_top_selection_amd import workloads as W
 pytestmark = pytest.mark.gpu
 
 DISTS = ["normal", "uniform", "levels", "const", "special"]
+SCALE = max(1, int(os.environ.get("DCPTOPK_FUZZ_SCALE", "1")))
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -63,7 +67,7 @@ def _compare(gb, gi, scores, ids, k, label):
         raise AssertionError(f"{label}: {len(bad)} rows differ, first {int(bad[0])}")
 
 
-@pytest.mark.parametrize("block", range(24))
+@pytest.mark.parametrize("block", range(24 * SCALE))
 def test_select_random_shapes(block):
     rng = np.random.default_rng(7000 + block)
     for case in range(25):
@@ -77,7 +81,7 @@ def test_select_random_shapes(block):
         _compare(gb, gi, g.scores, g.ids, k, label)
 
 
-@pytest.mark.parametrize("block", range(6))
+@pytest.mark.parametrize("block", range(6 * SCALE))
 def test_split_random_shapes(block):
     rng = np.random.default_rng(7100 + block)
     for case in range(20):
@@ -91,7 +95,7 @@ def test_split_random_shapes(block):
         _compare(gb, gi, g.scores, g.ids, k, label)
 
 
-@pytest.mark.parametrize("block", range(3))
+@pytest.mark.parametrize("block", range(3 * SCALE))
 def test_local_random_shapes(block):
     rng = np.random.default_rng(7200 + block)
     for case in range(30):
@@ -110,7 +114,7 @@ def test_local_random_shapes(block):
         assert np.array_equal(oi.cpu().numpy(), wi), label
 
 
-@pytest.mark.parametrize("block", range(3))
+@pytest.mark.parametrize("block", range(3 * SCALE))
 def test_fused_random_shapes(block):
     rng = np.random.default_rng(7300 + block)
     for case in range(20):
