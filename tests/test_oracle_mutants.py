@@ -32,6 +32,18 @@ def _key_truncated(scores):
     return (k >> np.uint32(4)) << np.uint32(4)
 
 
+def _key_zero_canonical(scores):
+    # -0 given the key of +0, as a float comparison would treat them
+    s = np.ascontiguousarray(scores, dtype=np.float32)
+    return _ORIG_SCORE_KEY(np.where(s == 0, np.float32(0.0), s))
+
+
+def _key_nan_top(scores):
+    # every NaN, whatever its sign, ordered above +inf
+    s = np.ascontiguousarray(scores, dtype=np.float32)
+    return np.where(np.isnan(s), np.uint32(0xFFFFFFFF), _ORIG_SCORE_KEY(s)).astype(np.uint32)
+
+
 def _key64_plain_id(scores, ids):
     hi = O.score_key(scores).astype(np.uint64) << np.uint64(32)
     return hi | np.ascontiguousarray(ids, np.int32).view(np.uint32).astype(np.uint64)
@@ -47,7 +59,8 @@ def _make_select(mistake):
             n_sel -= 1
         pad_bits = np.uint32(0) if mistake == "pad_zero" else np.uint32(0xFF800000)
         out_bits = np.full((rows, k), pad_bits, dtype=np.uint32)
-        out_ids = np.full((rows, k), np.int32(2**31 - 1), dtype=np.int32)
+        out_ids = np.full((rows, k), np.int32(-1) if mistake == "pad_id_minus_one" else np.int32(2**31 - 1),
+                          dtype=np.int32)
         key = O.sort_key64(scores, ids)
         if mistake == "last_position_wins":
             order = np.argsort(key, axis=1, kind="stable")[:, ::-1]
@@ -97,6 +110,8 @@ def _make_local(mistake):
         out_idx = np.full((rows, k), np.int32(2**31 - 1) if mistake == "pad_intmax" else np.int32(-1), np.int32)
         for t in range(rows):
             n = num_cols if lengths is None else int(min(max(int(lengths[t]), 0), num_cols))
+            if mistake == "lengths_off_by_one" and lengths is not None:
+                n = int(min(max(int(lengths[t]) - 1, 0), num_cols))
             key = O.score_key(scores[t, :n])
             if mistake == "ties_highest_column":
                 order = np.argsort(key, kind="stable")[::-1]
@@ -116,11 +131,14 @@ MUTANTS = {
     "key_no_negative_flip": ("score_key", _key_no_negative_flip),
     "key_sign_xor_only": ("score_key", _key_sign_xor_only),
     "key_truncated_low_bits": ("score_key", _key_truncated),
+    "key_zero_canonical": ("score_key", _key_zero_canonical),
+    "key_nan_top": ("score_key", _key_nan_top),
     "key64_plain_id": ("sort_key64", _key64_plain_id),
     "select_last_position_wins": ("select", _make_select("last_position_wins")),
     "select_score_order_output": ("select", _make_select("score_order_output")),
     "select_pad_zero": ("select", _make_select("pad_zero")),
     "select_off_by_one": ("select", _make_select("off_by_one")),
+    "select_pad_id_minus_one": ("select", _make_select("pad_id_minus_one")),
     "pack_no_rank_offset": ("pack", _make_pack("no_rank_offset")),
     "pack_invalid_keeps_score": ("pack", _make_pack("invalid_keeps_score")),
     "pack_wrong_row_start": ("pack", _make_pack("row_start_of_next_row")),
@@ -131,6 +149,7 @@ MUTANTS = {
     "local_score_order_output": ("local_topk", _make_local("score_order_output")),
     "local_pad_intmax": ("local_topk", _make_local("pad_intmax")),
     "local_ignores_lengths": ("local_topk", _make_local("ignores_lengths")),
+    "local_lengths_off_by_one": ("local_topk", _make_local("lengths_off_by_one")),
 }
 
 
