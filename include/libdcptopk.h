@@ -61,6 +61,13 @@ extern "C" {
  * (PR #47348, Benchmarks). */
 #define DCP_TOPK_MAX_CANDIDATES 16384
 
+/* Largest row count that one call of dcp_topk_select, dcp_topk_select_split,
+ * dcp_topk_merge_fused, dcp_topk_local or dcp_topk_pack accepts (more rows
+ * return DCP_TOPK_EUNSUPPORTED): one launch runs a workgroup of up to 1024
+ * threads per row in one grid, whose size in threads is a 32-bit count.  The
+ * chunked merges launch 1024 rows at a time and take any row count. */
+#define DCP_TOPK_MAX_ROWS 4194303
+
 /* Alignment the chunked merge requires of its workspace, in bytes. */
 #define DCP_TOPK_WORKSPACE_ALIGN 256
 
@@ -77,9 +84,10 @@ enum {
   DCP_TOPK_EINVAL = -1,       /* bad argument: null pointer, negative size,
                                  k < 1, misaligned or overlapping buffers */
   DCP_TOPK_EUNSUPPORTED = -2, /* valid but unsupported shape (num_cand or k
-                                 above DCP_TOPK_MAX_CANDIDATES, or a limit of
-                                 one entry point); the caller can fall back to
-                                 another selector */
+                                 above DCP_TOPK_MAX_CANDIDATES, rows above
+                                 DCP_TOPK_MAX_ROWS, or a limit of one entry
+                                 point); the caller can fall back to another
+                                 selector or split the rows */
   DCP_TOPK_EWORKSPACE = -3,   /* workspace too small or not 256-byte aligned */
   DCP_TOPK_EHIP = -4,         /* the HIP runtime rejected a launch */
   DCP_TOPK_ESCRATCH = -5      /* the shape needs more scratch than
@@ -104,7 +112,7 @@ enum {
  *   local_scores    device, fp32, rows x local_k with row stride src_row_stride
  *   local_idx       device, int32, same layout as local_scores
  *   src_row_stride  elements between consecutive rows, >= local_k
- *   row_starts      device, int32[rows]
+ *   row_starts      device, int32[rows]; rows <= DCP_TOPK_MAX_ROWS
  *   rank_offset     added to every valid id of this rank
  *   dst             device, 8-byte aligned; the first slot of this rank in
  *                   row 0 of a row-major gathered buffer (for DCP rank r of a
@@ -129,7 +137,7 @@ DCP_TOPK_API int dcp_topk_pack(const float* local_scores, const int32_t* local_i
  *   cand      device, 8-byte aligned, rows x num_cand candidates, row-major
  *             (rank r's candidates of a row at columns [r*local_k, (r+1)*local_k)
  *             when the buffer is a DCP gather; any order works)
- *   rows      query rows, >= 0
+ *   rows      query rows, 0 <= rows <= DCP_TOPK_MAX_ROWS
  *   num_cand  candidates per row, 0 <= num_cand <= DCP_TOPK_MAX_CANDIDATES
  *   k         candidates to select per row, >= 1 (k > num_cand pads)
  *   out       device, 8-byte aligned, rows x k candidates, row-major; must not
@@ -248,10 +256,11 @@ DCP_TOPK_API int dcp_topk_merge_chunked(const float* const* local_scores, const 
  *                 ranks); other values return DCP_TOPK_EUNSUPPORTED
  *
  * Limits (DCP_TOPK_EUNSUPPORTED): dcp <= DCP_TOPK_FUSED_MAX_RANKS, dcp *
- * local_k <= DCP_TOPK_MAX_CANDIDATES.  No workspace and no chunking: all rows
- * go in one launch.  The result is bit-identical to dcp_topk_merge_chunked
- * with the same arguments (so to dcp_topk_pack of every rank followed by
- * dcp_topk_select); out must not overlap any input (DCP_TOPK_EINVAL).
+ * local_k <= DCP_TOPK_MAX_CANDIDATES, rows <= DCP_TOPK_MAX_ROWS.  No
+ * workspace and no chunking: all rows go in one launch.  The result is
+ * bit-identical to dcp_topk_merge_chunked with the same arguments (so to
+ * dcp_topk_pack of every rank followed by dcp_topk_select); out must not
+ * overlap any input (DCP_TOPK_EINVAL).
  */
 DCP_TOPK_API int dcp_topk_merge_fused(const float* const* local_scores, const int32_t* const* local_idx,
                          const int32_t* const* row_starts, const int32_t* rank_offsets, int32_t dcp,
@@ -274,7 +283,8 @@ DCP_TOPK_API int dcp_topk_merge_fused(const float* const* local_scores, const in
  *                     score_row_stride (>= num_cols) elements
  *   lengths           device int32[rows], or NULL; len(t) = lengths[t]
  *                     clamped to [0, num_cols] (NULL: every column)
- *   num_cols          0 <= num_cols <= DCP_TOPK_MAX_CANDIDATES
+ *   num_cols          0 <= num_cols <= DCP_TOPK_MAX_CANDIDATES (rows: at most
+ *                     DCP_TOPK_MAX_ROWS)
  *   k                 1 <= k <= DCP_TOPK_MAX_CANDIDATES
  *   out_scores        device, fp32, rows x k, row stride out_row_stride (>= k)
  *   out_idx           device, int32, same layout as out_scores

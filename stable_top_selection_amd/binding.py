@@ -22,6 +22,7 @@ from .build import INCLUDE, LIB_PATH
 OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP, ESCRATCH = 0, -1, -2, -3, -4, -5
 MERGE_ROWS = 1024
 MAX_CANDIDATES = 16384
+MAX_ROWS = 4194303
 FUSED_MAX_RANKS = 16
 WORKSPACE_ALIGN = 256
 STATIC_SCRATCH_BYTES = 64 << 20

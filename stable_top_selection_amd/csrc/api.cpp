@@ -48,7 +48,8 @@ int check_select(const dcp_topk_cand* cand, int32_t rows, int32_t num_cand, int3
   if (rows == 0) return DCP_TOPK_OK;
   if (out == nullptr || (num_cand > 0 && cand == nullptr)) return DCP_TOPK_EINVAL;
   if (!aligned(out, kCandBytes) || (cand != nullptr && !aligned(cand, kCandBytes))) return DCP_TOPK_EINVAL;
-  if (num_cand > DCP_TOPK_MAX_CANDIDATES || k > DCP_TOPK_MAX_CANDIDATES) return DCP_TOPK_EUNSUPPORTED;
+  if (num_cand > DCP_TOPK_MAX_CANDIDATES || k > DCP_TOPK_MAX_CANDIDATES || rows > DCP_TOPK_MAX_ROWS)
+    return DCP_TOPK_EUNSUPPORTED;
   Span in_span, out_span;
   if (!strided_span(cand, rows, num_cand, num_cand, kCandBytes, &in_span)) return DCP_TOPK_EINVAL;
   if (!strided_span(out, rows, k, k, kCandBytes, &out_span)) return DCP_TOPK_EINVAL;
@@ -64,6 +65,7 @@ int check_pack(const float* scores, const int32_t* idx, int64_t src_row_stride, 
   if (src_row_stride < local_k || dst_row_stride < local_k) return DCP_TOPK_EINVAL;
   if (!aligned(scores, 4) || !aligned(idx, 4) || !aligned(row_starts, 4) || !aligned(dst, kCandBytes))
     return DCP_TOPK_EINVAL;
+  if (rows > DCP_TOPK_MAX_ROWS) return DCP_TOPK_EUNSUPPORTED;
   Span s, i, r, d;
   if (!strided_span(scores, rows, local_k, src_row_stride, 4, &s) ||
       !strided_span(idx, rows, local_k, src_row_stride, 4, &i) || !strided_span(row_starts, rows, 1, 1, 4, &r) ||
@@ -253,7 +255,8 @@ int dcp_topk_merge_fused(const float* const* local_scores, const int32_t* const*
   if (local_scores == nullptr || local_idx == nullptr || row_starts == nullptr || rank_offsets == nullptr)
     return DCP_TOPK_EINVAL;
   if (dcp > dcptopk::kMaxFusedRanks || local_k % 64 != 0 ||
-      static_cast<int64_t>(dcp) * local_k > DCP_TOPK_MAX_CANDIDATES || k > DCP_TOPK_MAX_CANDIDATES)
+      static_cast<int64_t>(dcp) * local_k > DCP_TOPK_MAX_CANDIDATES || k > DCP_TOPK_MAX_CANDIDATES ||
+      rows > DCP_TOPK_MAX_ROWS)
     return DCP_TOPK_EUNSUPPORTED;
   if (rows == 0) return DCP_TOPK_OK;
   if (out == nullptr || !aligned(out, kCandBytes)) return DCP_TOPK_EINVAL;
@@ -272,7 +275,8 @@ int dcp_topk_local(const float* scores, int64_t score_row_stride, const int32_t*
                    int32_t num_cols, int32_t k, float* out_scores, int32_t* out_idx, int64_t out_row_stride,
                    hipStream_t stream) {
   if (rows < 0 || num_cols < 0 || k < 1) return DCP_TOPK_EINVAL;
-  if (num_cols > DCP_TOPK_MAX_CANDIDATES || k > DCP_TOPK_MAX_CANDIDATES) return DCP_TOPK_EUNSUPPORTED;
+  if (num_cols > DCP_TOPK_MAX_CANDIDATES || k > DCP_TOPK_MAX_CANDIDATES || rows > DCP_TOPK_MAX_ROWS)
+    return DCP_TOPK_EUNSUPPORTED;
   if (rows == 0) return DCP_TOPK_OK;
   if (out_scores == nullptr || out_idx == nullptr || (num_cols > 0 && scores == nullptr)) return DCP_TOPK_EINVAL;
   if (score_row_stride < num_cols || out_row_stride < k) return DCP_TOPK_EINVAL;

@@ -95,6 +95,26 @@ def test_select_argument_checks(lib):
     assert s(P(DEV_A), 4, 64, 16, P(DEV_A + 64 * 8), None) == B.EINVAL
 
 
+def test_row_limit(lib):
+    """Past DCP_TOPK_MAX_ROWS rows every single-launch entry point returns
+    DCP_TOPK_EUNSUPPORTED before any launch (the grid's thread count is a
+    32-bit number); the chunked merge takes any row count."""
+    big = B.MAX_ROWS + 1
+    far = 0x7F8000000000  # fake outputs well past the fake inputs' spans
+    assert lib.dcp_topk_select(P(DEV_A), big, 1, 1, P(far), None) == B.EUNSUPPORTED
+    assert lib.dcp_topk_select(P(DEV_A), big, -1, 1, P(far), None) == B.EINVAL  # checked first
+    ws = P(far + 0x100000000)
+    assert lib.dcp_topk_select_split(P(DEV_A), big, 64, 1, 2, ws, 1 << 30, P(far), None) == B.EUNSUPPORTED
+    assert lib.dcp_topk_pack(P(DEV_A), P(DEV_A + 0x100000000), 1, P(DEV_A + 0x200000000), 0, big, 1, P(far), 1,
+                             None) == B.EUNSUPPORTED
+    ranks = _rank_arrays(1)
+    assert lib.dcp_topk_merge_fused(*ranks, 1, big, 64, 1, P(far), None) == B.EUNSUPPORTED
+    assert lib.dcp_topk_local(P(DEV_A), 1, None, big, 1, 1, P(far), P(far + 0x100000000), 1, None) == B.EUNSUPPORTED
+    # the limit itself is accepted by the checks: rows == 0 aside, a call that
+    # passes every check would launch, so only a check that fails later is used
+    assert lib.dcp_topk_select(P(DEV_A), B.MAX_ROWS, 1, 1, P(DEV_A + 8), None) == B.EINVAL  # overlap, not the limit
+
+
 def test_pack_argument_checks(lib):
     p = lib.dcp_topk_pack
     a, b, c, d = P(DEV_A), P(DEV_A + 0x100000), P(DEV_A + 0x200000), P(DEV_B)
