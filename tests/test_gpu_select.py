@@ -266,6 +266,26 @@ def test_row_offsets_beyond_2_gib():
     torch.cuda.empty_cache()
 
 
+def test_max_rows():
+    """DCP_TOPK_MAX_ROWS rows (4,194,303) of 3 candidates, k 2: the largest grid
+    one select launch takes (256 threads per row, about 1.07e9 threads).  Every
+    row is checked against the oracle, with score ties in a tenth of the rows;
+    one row more is refused before any launch."""
+    rows = B.MAX_ROWS
+    rng = np.random.default_rng(4242)
+    scores = rng.standard_normal((rows, 3), dtype=np.float32)
+    tied = rng.random(rows) < 0.1
+    scores[tied, 2] = scores[tied, 0]
+    ids = rng.integers(0, 1 << 20, size=(rows, 3), dtype=np.int32)
+    assert_select_parity(scores, ids, 2, "max rows")
+    cand = torch.zeros((rows + 1, 3, 2), dtype=torch.int32, device=DEV)
+    with pytest.raises(B.DcpTopkError) as e:
+        B.select(cand, 2)
+    assert e.value.status == B.EUNSUPPORTED
+    del cand
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("c,k", [(1000, 300), (2048, 2047), (300, 1)])
 def test_rows_of_one_repeated_candidate(c, k):
     """Every candidate identical (same score bits and id): the first k
