@@ -140,6 +140,29 @@ def test_local_errors():
     assert e.value.status == B.EINVAL
 
 
+def test_local_max_rows():
+    """DCP_TOPK_MAX_ROWS rows (4,194,303) of 3 columns with per-row lengths, k 2:
+    the largest grid one launch takes.  200,000 seeded rows are checked
+    against the oracle; one row more is refused before any launch."""
+    rows = B.MAX_ROWS
+    rng = np.random.default_rng(4343)
+    scores = rng.standard_normal((rows, 3), dtype=np.float32)
+    lengths = rng.integers(-1, 5, size=rows, dtype=np.int32)
+    os_, oi = B.local_topk(to_dev(scores), 2, lengths=to_dev(lengths))
+    torch.cuda.synchronize()
+    pick = np.sort(rng.choice(rows, 200000, replace=False))
+    ws, wi = O.local_topk(scores[pick], 2, lengths[pick])
+    assert np.array_equal(os_.cpu().numpy()[pick].view(np.uint32), ws.view(np.uint32))
+    assert np.array_equal(oi.cpu().numpy()[pick], wi)
+    del os_, oi
+    big = torch.zeros((rows + 1, 3), dtype=torch.float32, device=DEV)
+    with pytest.raises(B.DcpTopkError) as e:
+        B.local_topk(big, 2)
+    assert e.value.status == B.EUNSUPPORTED
+    del big
+    torch.cuda.empty_cache()
+
+
 def test_local_graph_replay_with_changing_inputs():
     """Captured into a HIP graph once; before each replay the scores and the
     per-row lengths are overwritten in place (eager copies, a synchronisation
