@@ -54,6 +54,35 @@ def test_pack_parity(rows, local_k, column, width):
     assert np.all(o[:, untouched] == 123), "pack wrote outside its columns"
 
 
+def test_pack_max_rows():
+    """dcp_topk_pack over DCP_TOPK_MAX_ROWS rows (4,194,303) of 2 slots into
+    columns 1-2 of a 4-column buffer, with invalid slots: every row against
+    the oracle; one row more is refused before any launch."""
+    rows, local_k, width = B.MAX_ROWS, 2, 4
+    rng = np.random.default_rng(4444)
+    scores = rng.standard_normal((rows, local_k), dtype=np.float32)
+    idx = rng.integers(-1, 4096, size=(rows, local_k), dtype=np.int32)
+    starts = rng.integers(0, 1 << 20, size=rows, dtype=np.int32)
+    dst = torch.full((rows, width, 2), 123, dtype=torch.int32, device=DEV)
+    B.pack(to_dev(scores), to_dev(idx), to_dev(starts), 5 << 22, dst, column=1)
+    torch.cuda.synchronize()
+    want_s, want_i = O.pack(scores, idx, starts, 5 << 22)
+    o = dst.cpu().numpy()
+    assert np.array_equal(o[:, 1:3, 0].view(np.uint32), want_s.view(np.uint32))
+    assert np.array_equal(o[:, 1:3, 1], want_i)
+    assert np.all(o[:, 0] == 123) and np.all(o[:, 3] == 123), "pack wrote outside its columns"
+    del dst
+    one_more = torch.zeros((rows + 1, local_k), dtype=torch.float32, device=DEV)
+    one_more_idx = torch.zeros((rows + 1, local_k), dtype=torch.int32, device=DEV)
+    one_more_starts = torch.zeros((rows + 1,), dtype=torch.int32, device=DEV)
+    one_more_dst = torch.zeros((rows + 1, local_k, 2), dtype=torch.int32, device=DEV)
+    with pytest.raises(B.DcpTopkError) as e:
+        B.pack(one_more, one_more_idx, one_more_starts, 0, one_more_dst)
+    assert e.value.status == B.EUNSUPPORTED
+    del one_more, one_more_idx, one_more_starts, one_more_dst
+    torch.cuda.empty_cache()
+
+
 def test_pack_wraps_and_marks_invalid():
     scores = torch.tensor([[1.5, -2.0, 3.0, 4.0]], dtype=torch.float32, device=DEV)
     idx = torch.tensor([[2**31 - 10, -1, 0, -7]], dtype=torch.int32, device=DEV)
