@@ -170,6 +170,38 @@ def test_fused_equals_chunked_on_ties():
     _parity(sh, 2048, "ties with shared ids")
 
 
+def test_fused_max_rows():
+    """DCP_TOPK_MAX_ROWS rows (4,194,303) in one launch: DCP 2 x local K 64, k 5,
+    from a seeded 4096-row block with invalid slots tiled 1024 times on the
+    device (1 GiB per rank array).  Whole repeats of the block (the first,
+    one in the middle, the last full one) are checked against the oracle's
+    result for the block; the tiled 4,194,304 rows, one more than the limit,
+    are refused before any launch."""
+    block_rows, dcp, local_k, k, reps = 4096, 2, 64, 5, 1024
+    sh = _random_shards(block_rows, dcp, local_k, seed=4545, invalid_frac=0.05)
+    want_s, want_i = O.merge(sh.scores, sh.local_idx, sh.row_starts, sh.rank_offsets, k)
+    want = np.stack([want_s.view(np.int32), want_i], axis=-1)
+    sc = [to_dev(sh.scores[r]).repeat(reps, 1) for r in range(dcp)]
+    ix = [to_dev(sh.local_idx[r]).repeat(reps, 1) for r in range(dcp)]
+    rs = [to_dev(sh.row_starts[r]).repeat(reps) for r in range(dcp)]
+    offs = [int(x) for x in sh.rank_offsets]
+    rows = B.MAX_ROWS
+    assert sc[0].shape[0] == rows + 1
+    out = B.merge_fused([t[:rows] for t in sc], [t[:rows] for t in ix], [t[:rows] for t in rs], offs, k)
+    torch.cuda.synchronize()
+    for r in (0, reps // 2, reps - 2):
+        got = out[r * block_rows:(r + 1) * block_rows].cpu().numpy()
+        assert np.array_equal(got, want), f"block repeat {r} differs"
+    last = out[(reps - 1) * block_rows:].cpu().numpy()
+    assert np.array_equal(last, want[:block_rows - 1]), "the last, partial repeat differs"
+    del out
+    with pytest.raises(B.DcpTopkError) as e:
+        B.merge_fused(sc, ix, rs, offs, k)
+    assert e.value.status == B.EUNSUPPORTED
+    del sc, ix, rs
+    torch.cuda.empty_cache()
+
+
 def test_fused_graph_replay():
     """Captured into a HIP graph and replayed with new contents in the same
     rank arrays before each replay (eager copies and a synchronisation in
