@@ -121,6 +121,33 @@ def test_merge_chunked_full_prefill():
     _merge_parity(sh, sh.k, sh.name)
 
 
+def test_merge_chunked_past_the_single_launch_row_limit():
+    """The chunked merge launches 1024 rows at a time, so it takes more rows
+    than one launch may: 4,194,816 rows (DCP_TOPK_MAX_ROWS + 513, a last chunk
+    of 512) of DCP 1 x local K 64, k 5, from a seeded 4096-row block with
+    invalid slots tiled on the device.  Whole repeats of the block and the
+    last, partial one are checked against the oracle's result for the block."""
+    block_rows, local_k, k = 4096, 64, 5
+    rows = B.MAX_ROWS + 513
+    reps = -(-rows // block_rows)
+    sh = _random_shards(block_rows, 1, local_k, seed=4646, invalid_frac=0.05)
+    want_s, want_i = O.merge(sh.scores, sh.local_idx, sh.row_starts, sh.rank_offsets, k)
+    want = np.stack([want_s.view(np.int32), want_i], axis=-1)
+    sc = to_dev(sh.scores[0]).repeat(reps, 1)[:rows]
+    ix = to_dev(sh.local_idx[0]).repeat(reps, 1)[:rows]
+    rs = to_dev(sh.row_starts[0]).repeat(reps)[:rows]
+    out = B.merge_chunked([sc], [ix], [rs], [int(sh.rank_offsets[0])], k)
+    torch.cuda.synchronize()
+    assert out.shape[0] == rows > B.MAX_ROWS
+    for r in (0, reps // 2, reps - 2):
+        got = out[r * block_rows:(r + 1) * block_rows].cpu().numpy()
+        assert np.array_equal(got, want), f"block repeat {r} differs"
+    tail = rows - (reps - 1) * block_rows
+    assert np.array_equal(out[(reps - 1) * block_rows:].cpu().numpy(), want[:tail]), "the last, partial repeat differs"
+    del sc, ix, rs, out
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("rows,dcp,local_k,k", [(37, 3, 100, 50), (20, 9, 64, 100), (11, 2, 7, 20),
                                                (1030, 4, 33, 1), (6, 16, 1024, 2048), (4, 4, 0, 3)])
 def test_merge_chunked_ragged(rows, dcp, local_k, k):
